@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Throughput of one data-parallel rank's ZeRO step on its 1/N shard.
+
+Default workload: the Llama-3-8B-shaped parameter list (psi = 8,030,261,248)
+at N = 8, rank 0's shard of S = 1,003,782,656 parameters, fp16 contributions
+~N(0, 1e-3) x 65536, AdamW lr 3e-4, wd 0.1, global clip at 1.0 (the other
+seven ranks' squared norm stood in by a host scalar).
+
+A step is one pass of the whole path: zero_reduce_check (reduce N fp16 rows,
+unscale, overflow flag, exact squared norm, clip / skip decision) then
+zero_adam_apply (AdamW on fp32 master, m, v and the fp16 slot write); this is
+exactly what zero_reduce_adam_step enqueues.  Inputs are resident in HBM when
+the timed region starts; every timed step is applied (no skip).
+
+Prints one JSON line.  Fields beyond the common ones:
+  roofline      the dominant kernel's algorithmic bytes per launch over its
+                average HIP-event duration, against the 8 TB/s HBM peak
+  kernels       the same figures for both kernels
+  cpu_baseline  the CPU oracle timed on a bounded window of the same shard
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ("zero_sharded_optimizer_rank_amd/csrc/zero_kernels.hip",
+                  "zero_sharded_optimizer_rank_amd/csrc/zero_internal.h")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def bytes_per_param(n: int):
+    """Algorithmic bytes per shard element of each kernel on an applied step."""
+    k1 = 2 * n + 4   # read N fp16 contributions, write fp32 g
+    k2 = 16 + 14     # read g, master, m, v; write master, m, v and the fp16 slot
+    return k1, k2
+
+
+def traffic_for(workload: str, kernel: str):
+    """Counter-derived HBM bytes per launch, if recorded for the current
+    kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle as it is, on rank 0's first 2^25 shard elements, repeated
+    for about `seconds`; input generation is outside the timing."""
+    import oracle
+    from oracle import run as orun
+
+    p = orun.workload_plan(w)
+    n = min(1 << 25, p.shard)
+    c = orun.shard_contrib(w, p, 0, 1, w.loss_scale0, 0, n)
+    pm, m, v, h = orun.initial_state(w, p, 0, 0, n)
+    other_sq = w.other_sq(p.real(0)) if w.other_ranks_from_config else 0.0
+    reps, t0 = 0, time.perf_counter()
+    t_applied = 0
+    while True:
+        sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, t_applied + 1,
+                                 w.world_size, w.loss_scale0)
+        out = oracle.shard_step(c, pm, m, v, h, sc, w.max_grad_norm, other_sq=other_sq)
+        pm, m, v, h = out.p, out.m, out.v, out.h
+        t_applied += 0 if out.fin.skip else 1
+        reps += 1
+        el = time.perf_counter() - t0
+        if reps >= 2 and el >= seconds:
+            break
+    return {"value": n * reps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{w.name} rank 0 shard elements [0, {n}) x {w.world_size} contributions, "
+                      f"{reps} oracle steps (numpy, one thread), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b")
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-bytes", type=float, default=4e9,
+                    help="bytes of the calibration copy timed next to the step (0: skip)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print("bench.py measures the shard step on one GPU only; --gpus must be 1 "
+              "(the multi-GPU exchange around the step is not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from zero_sharded_optimizer_rank_amd import abi
+    from zero_sharded_optimizer_rank_amd.shard import DeviceShard
+
+    abi.lib()
+    w = synth.BY_NAME[a.workload]
+    dev = DeviceShard(w, a.rank)
+    stream = dev.stream
+    n = w.world_size
+    real = abi.zero_plan_real(dev.full_plan, a.rank)
+    other_sq = w.other_sq(real) if w.other_ranks_from_config else 0.0
+    t_setup = time.perf_counter()
+    dev.load_initial_state()
+    dev.load_contributions(1, w.loss_scale0)
+    setup_s = time.perf_counter() - t_setup
+
+    def args_for(t):
+        return dev.args(t, w.loss_scale0, other_sq=other_sq)
+
+    for i in range(a.warmup):
+        dev.reduce_check(args_for(i + 1))
+        dev.adam_apply(args_for(i + 1))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        args = args_for(a.warmup + i + 1)
+        ev[i][0].record(stream)
+        dev.reduce_check(args)
+        ev[i][1].record(stream)
+        dev.adam_apply(args)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    res = dev.result()
+    if res.skip:
+        raise RuntimeError("a timed step was skipped")
+    k1_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / a.steps
+    k2_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / a.steps
+    ms_per_step = wall * 1e3 / a.steps
+
+    S = dev.count
+    b1, b2 = bytes_per_param(n)
+    kernels = {
+        "k1_reduce_check": {"ms": k1_ms, "bytes_per_param": b1, "bytes": b1 * S,
+                            "gbps": b1 * S / (k1_ms * 1e6)},
+        "k2_adam": {"ms": k2_ms, "bytes_per_param": b2, "bytes": b2 * S,
+                    "gbps": b2 * S / (k2_ms * 1e6)},
+    }
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    traffic = traffic_for(w.name, dom)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["gbps"],
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": kernels[dom]["gbps"] / HBM_PEAK_GBPS, "traffic": traffic}
+
+    calib = None
+    if a.calib_bytes > 0:
+        import ctypes
+        from zero_sharded_optimizer_rank_amd.build import CALIB_LIB
+        cl = ctypes.CDLL(CALIB_LIB)
+        cl.zero_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_int, ctypes.c_void_p]
+        nb = int(a.calib_bytes) // 16 * 16
+        del dev
+        torch.cuda.empty_cache()
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        best = None
+        for blocks in (2048, 4096, 8192):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for rep in range(4):
+                if rep == 1:
+                    e0.record(stream)
+                rc = cl.zero_calib_copy(src.data_ptr(), dst.data_ptr(), nb, blocks,
+                                        stream.cuda_stream)
+                assert rc == 0
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gbps = 2 * nb * 3 / (e0.elapsed_time(e1) * 1e6)
+            best = gbps if best is None else max(best, gbps)
+        calib = {"copy_gbps": best, "bytes": nb}
+
+    out = {
+        "metric": "params updated/sec + achieved HBM GB/s, Llama-3-8B shard step N=8"
+        if w.name == "llama3_8b" else f"params updated/sec + achieved HBM GB/s, {w.name} shard step",
+        "value": real / (ms_per_step / 1e3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: rank {a.rank} of N={n}, shard S={S} "
+                               f"(psi={w.psi}), fp16 contributions, fp32 master/m/v",
+                   "world_size_simulated": n, "shard": S, "psi": w.psi},
+        "hbm_gbps_step": (2 * n + 34) * S / (ms_per_step * 1e6),
+        "hbm_gbps_step_floor_bytes": (2 * n + 26) * S / (ms_per_step * 1e6),
+        "roofline": roofline,
+        "kernels": kernels,
+        "calibration_copy": calib,
+        "setup_s": setup_s,
+        "kernel_hash": kernel_hash(),
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,259 @@
+/*
+ * zero_shard.h -- C ABI of one data-parallel rank's ZeRO step on its 1/N shard,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The step (pages: "10.6 ZeRO 与 FSDP", §10.6.1-§10.6.3; "第13篇 · ZeRO", §3.2;
+ * "ZeRO-1/2/3 分别优化了什么", sections on ZeRO-1 and ZeRO-2):
+ *   1. reduce side of the gradient reduce-scatter, done locally: sum the N
+ *      ranks' fp16 contributions to this rank's slice in rank order 0..N-1
+ *      with fp32 accumulation, then average and unscale by the loss scale;
+ *   2. detect inf/NaN and form the exact partial squared L2 norm; combine it
+ *      with the other ranks' into the clip coefficient and the skip decision;
+ *   3. mixed-precision Adam/AdamW on the fp32 master, m and v of the shard;
+ *   4. cast the new master to fp16 into this rank's slot of the flat
+ *      parameter buffer (the all-gather's local slot).
+ *
+ * Conventions for every entry point:
+ *   - int-returning calls return ZERO_OK (0) or a negative zero_status; the
+ *     message of the last failure on the calling thread is zero_last_error().
+ *   - Device calls are asynchronous on the given HIP stream; results in
+ *     device memory are readable once the caller synchronises that stream.
+ *   - The library allocates no memory.  Every buffer is owned by the caller
+ *     and must stay alive until the stream has passed the call.
+ *   - Pointers marked "device" are HIP device pointers; "host" are host
+ *     pointers read before the call returns.
+ *   - A workspace or result buffer used by one call must not be used by an
+ *     overlapping call on another stream.
+ *
+ * The hyperparameters arrive as fp64 and are rounded to fp32 once on the host
+ * (1 - beta1 is f32(0.1), not 1f - 0.9f); beta^t is a product of t fp64
+ * factors.  The Adam sequence is Kingma & Ba Adam with bias correction, eps
+ * outside the square root, and decoupled weight decay on the old parameter;
+ * each fp32 operation is rounded separately (no fused multiply-add), with
+ * correctly rounded division and square root.
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum zero_status {
+  ZERO_OK = 0,
+  ZERO_EINVAL = -1, /* bad argument value or size */
+  ZERO_EALIGN = -2, /* a pointer lacks the alignment stated below */
+  ZERO_ENOSPC = -3, /* a caller buffer is too small */
+  ZERO_EHIP = -4    /* a HIP runtime call or kernel launch failed */
+};
+
+/* Largest N the device calls accept (contribution pointers travel as kernel
+ * arguments). */
+#define ZERO_MAX_RANKS 64
+/* Largest shard, in elements, the device calls accept. */
+#define ZERO_MAX_SHARD ((int64_t)0x7FFFFFF8)
+
+typedef struct zero_plan {
+  int64_t psi;        /* real parameters in the flat buffer */
+  int64_t world_size; /* N */
+  int64_t align;      /* shard size is a multiple of this many elements */
+  int64_t shard;      /* S: elements owned by each rank, padding included */
+  int64_t psi_padded; /* N * S */
+} zero_plan_t;
+
+/*
+ * zero_plan: flatten a tensor list and partition it into N equal shards.
+ * Pages: "第13篇 · ZeRO", §2.1 (gradients gathered into one flat buffer) and
+ * §3.2 (process i stores and updates partition i); "10.6 ZeRO 与 FSDP",
+ * §10.6.2 (each GPU owns and updates 1/N).
+ *   numels        host [n_tensors], element counts (>= 0), in flat order
+ *   world_size    N, >= 1
+ *   align_elems   >= 1; S = ceil(psi / N) rounded up to a multiple of it
+ *   plan_out      host, filled on success
+ *   offsets_out   host [n_tensors], caller-owned: exclusive prefix sum of
+ *                 numels (tensor i starts at flat index offsets_out[i]);
+ *                 may be NULL
+ * Rank r owns flat [r*S, (r+1)*S); flat indexes >= psi are padding, which
+ * holds zero contributions and zero state and stays zero.  Pure host code.
+ * Errors: ZERO_EINVAL for a NULL numels with n_tensors > 0, n_tensors < 0, a
+ * negative numel, world_size < 1, align_elems < 1 or an int64 overflow.
+ */
+int zero_plan(const int64_t* numels, int32_t n_tensors, int32_t world_size, int32_t align_elems,
+              zero_plan_t* plan_out, int64_t* offsets_out);
+
+/* Real (non-padding) elements in rank's shard: clamp(psi - rank*S, 0, S);
+ * -1 for a NULL plan or a rank outside [0, N). */
+int64_t zero_plan_real(const zero_plan_t* plan, int32_t rank);
+
+typedef struct zero_segment {
+  int32_t tensor;       /* index into the tensor list */
+  int32_t reserved;
+  int64_t tensor_begin; /* first element of the tensor inside this shard */
+  int64_t shard_begin;  /* where that element sits in the shard */
+  int64_t length;       /* elements in this piece */
+} zero_segment_t;
+
+/*
+ * zero_plan_segments: the pieces of each tensor that fall in rank's shard,
+ * in flat order (same pages as zero_plan).
+ *   offsets  host [n_tensors] as returned by zero_plan
+ *   out      host [cap], caller-owned; *n_out receives the piece count
+ * Errors: ZERO_EINVAL for NULL arguments or a bad rank; ZERO_ENOSPC when more
+ * than cap pieces exist (*n_out still receives the count).
+ */
+int zero_plan_segments(const zero_plan_t* plan, const int64_t* numels, const int64_t* offsets,
+                       int32_t n_tensors, int32_t rank, zero_segment_t* out, int32_t cap,
+                       int32_t* n_out);
+
+/*
+ * zero_state_bytes: model-state bytes per rank for mixed-precision training
+ * with K bytes of optimizer state per parameter (K = 12 for Adam: fp32
+ * master, momentum and variance).
+ *   stage 0 (plain data parallel): (4 + K) psi
+ *   stage 1 (optimizer states sharded): 4 psi + K psi / N
+ *   stage 2 (+ gradients sharded): 2 psi + (2 + K) psi / N
+ *   stage 3 (+ parameters sharded): (4 + K) psi / N
+ * Pages: "ZeRO-1/2/3 分别优化了什么" (训练状态的显存构成 and each stage's
+ * 显存节省); "第13篇 · ZeRO", §2.2 and §3.2; "10.6 ZeRO 与 FSDP", table 10-2.
+ * Returns the byte count, or -1.0 for stage outside 0..3, psi < 0, n < 1,
+ * k < 0 or a NaN argument.
+ */
+double zero_state_bytes(int32_t stage, double psi, double n, double k);
+
+typedef struct zero_step_args {
+  double lr, beta1, beta2, eps;
+  double weight_decay;   /* decoupled (AdamW); 0 gives Adam */
+  double max_grad_norm;  /* <= 0: no clipping */
+  double loss_scale;     /* the loss scale the contributions carry, > 0 */
+  int64_t step;          /* 1-based Adam step t of this update if it applies */
+  double other_sq;       /* other ranks' squared norm as a plain fp64 value, >= 0 */
+  uint64_t other_q_lo;   /* other ranks' exact sum of squared fp32 sums, in */
+  uint64_t other_q_hi;   /*   units of 2^-48 (128-bit; an exact all-reduce) */
+  int32_t other_overflow; /* nonzero: another rank saw inf/NaN */
+  int32_t reserved;
+} zero_step_args_t;
+
+/*
+ * Written to device memory by zero_reduce_check / zero_finalize, read by
+ * zero_adam_apply.  With Q = sum over the shard of acc_j^2 in units of 2^-48
+ * (exact), inv = 1 / (N * loss_scale) in fp64 and f64() one rounding to
+ * nearest even:
+ *   own_sq    = ((f64(Q) * 2^-48) * inv) * inv
+ *   total_sq  = ((f64(Q + other_q) * 2^-48) * inv) * inv + other_sq
+ *   norm      = sqrt(total_sq)
+ *   clip_coef = f32(min(1, max_grad_norm / (norm + 1e-6))), or 1 without clipping
+ *   skip      = overflow || other_overflow || Q + other_q >= 2^128
+ */
+typedef struct zero_step_result {
+  uint64_t own_q_lo, own_q_hi;
+  double own_sq;
+  double total_sq;
+  double norm;
+  float clip_coef;
+  int32_t overflow; /* this shard's sums held inf or NaN */
+  int32_t skip;     /* the update was (or will be) skipped */
+  int32_t reserved;
+} zero_step_result_t;
+
+/* Bytes of workspace zero_reduce_check needs (fixed; 256 KiB + 256).  The
+ * workspace must be zero-filled before its first use; every call leaves it
+ * ready for the next. */
+size_t zero_workspace_bytes(void);
+
+/*
+ * zero_reduce_check: step 1 and 2 for rank's shard of S = plan->shard elements.
+ * Pages: "10.6 ZeRO 与 FSDP", §10.6.1 (reduce-scatter: reduce, keep 1/N) and
+ * §10.6.2 step 2; "ZeRO-1/2/3 分别优化了什么", ZeRO-2 (each card receives the
+ * average of all cards' gradients); the tutorial's "gradient_clipping": 1.0
+ * (§4.2) and loss scaling (§4.3).
+ *   contrib    host [N] of device pointers; contrib[r] holds rank r's S fp16
+ *              values (IEEE binary16 bit patterns) for this shard; 16-byte aligned
+ *   args       host; loss_scale, max_grad_norm, other_* are read
+ *   grad_out   device [S] fp32, 16-byte aligned: g_j = f32(acc_j * f32(inv))
+ *              with acc_j = (...((+0 + c_0j) + c_1j) + ...) + c_(N-1)j in fp32
+ *   workspace  device, >= zero_workspace_bytes(), 16-byte aligned, zeroed once
+ *   dev_result device, 8-byte aligned; fully written
+ * Errors: ZERO_EINVAL (N outside 1..ZERO_MAX_RANKS, bad rank, S outside
+ * 0..ZERO_MAX_SHARD, NULL pointers, loss_scale <= 0, other_sq < 0 or not
+ * finite, max_grad_norm NaN), ZERO_EALIGN, ZERO_ENOSPC (workspace), ZERO_EHIP.
+ */
+int zero_reduce_check(const zero_plan_t* plan, int32_t rank, const uint16_t* const* contrib,
+                      const zero_step_args_t* args, float* grad_out, void* workspace,
+                      size_t ws_bytes, zero_step_result_t* dev_result, hipStream_t stream);
+
+/*
+ * zero_finalize: recompute norm, clip_coef and skip of dev_result from its
+ * own_q and overflow and from new args (other ranks' values).  The host uses
+ * it to stand in for the all-reduce of {Q, overflow} when it simulates
+ * several ranks.  dev_result: device, written by an earlier zero_reduce_check.
+ * Errors: as zero_reduce_check for args and dev_result.
+ */
+int zero_finalize(const zero_plan_t* plan, const zero_step_args_t* args,
+                  zero_step_result_t* dev_result, hipStream_t stream);
+
+/*
+ * zero_adam_apply: steps 3 and 4 unless dev_result->skip.
+ * Pages: "10.6 ZeRO 与 FSDP", §10.6.2 step 3 (local 1/N optimizer state and
+ * gradient update the local 1/N parameters) and step 4 (all-gather of the
+ * updated parameters); "第13篇 · ZeRO", §2.2 (fp32 master, momentum, variance).
+ *   grad                device [S] fp32 from zero_reduce_check, 16-byte aligned
+ *   master, m, v        device [S] fp32, in place, 16-byte aligned
+ *   param16_slot        device [S] fp16 bit patterns = flat16 + rank * S;
+ *                       2-byte aligned (any shard offset)
+ *   args                host; lr, betas, eps, weight_decay, step, loss_scale
+ *   dev_result          device; clip_coef and skip are read
+ * Per element, one rounding per line:
+ *   gc = g*c;  m = b1*m + (1-b1)*gc;  v = b2*v + (1-b2)*(gc*gc);
+ *   den = sqrt(v)/sqrt(1-b2^t) + eps;  u = (m/den) * (lr/(1-b1^t));
+ *   p = p*(1-lr*wd) - u;  slot = fp16(p) rounded to nearest even.
+ * On a skipped step nothing is written.
+ * Errors: ZERO_EINVAL (bad args: lr or eps negative or NaN, a beta outside
+ * [0, 1), step < 1, NULL pointers), ZERO_EALIGN, ZERO_EHIP.
+ */
+int zero_adam_apply(const zero_plan_t* plan, int32_t rank, const float* grad, float* master,
+                    float* m, float* v, uint16_t* param16_slot, const zero_step_args_t* args,
+                    const zero_step_result_t* dev_result, hipStream_t stream);
+
+/*
+ * zero_reduce_adam_step: the whole step, zero_reduce_check then
+ * zero_adam_apply, enqueued back to back with no host synchronisation.
+ * Arguments and errors as the two calls; nothing is launched if any argument
+ * check fails.
+ */
+int zero_reduce_adam_step(const zero_plan_t* plan, int32_t rank, const uint16_t* const* contrib,
+                          float* master, float* m, float* v, uint16_t* param16_slot,
+                          float* grad_out, void* workspace, size_t ws_bytes,
+                          const zero_step_args_t* args, zero_step_result_t* dev_result,
+                          hipStream_t stream);
+
+typedef struct zero_scaler {
+  double scale;            /* current loss scale */
+  double growth, backoff;  /* e.g. 2.0 and 0.5 */
+  double min_scale;        /* floor, e.g. 1.0 */
+  int64_t growth_interval; /* clean steps before growth, e.g. 1000 */
+  int64_t good_steps;      /* clean steps since the last change */
+  int64_t t;               /* Adam steps applied so far */
+} zero_scaler_t;
+
+/*
+ * zero_scaler_update: dynamic loss scaling after a step (host).  The tutorial
+ * (§4.3) says fp16 training may need loss scaling; reading: on a skipped step
+ * scale = max(scale*backoff, min_scale) and good_steps = 0; otherwise t += 1
+ * and after growth_interval clean steps in a row scale *= growth.
+ * Errors: ZERO_EINVAL for NULL or a non-positive scale.
+ */
+int zero_scaler_update(zero_scaler_t* s, int32_t skipped);
+
+/* Message of the last failure on this thread ("" if none). */
+const char* zero_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_SHARD_H */

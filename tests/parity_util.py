@@ -1,0 +1,140 @@
+"""Helpers for the GPU parity tests: run a workload window on the GPU through
+the C ABI and on the CPU through the oracle, on the same seeded inputs, and
+compare.
+
+Acceptance bar: the reduced gradient, the exact squared-norm integer, the
+fp64 norm values, the clip coefficient and the overflow / skip decisions are
+bit-exact; fp32 master, m and v are within 1e-6 relative error with zeros
+matching exactly; the fp16 slot is within 1 ulp.  Bitwise mismatch counts are
+reported and also required to be zero, since both sides run the same rounded
+fp32 sequence.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+import oracle
+import synth
+from oracle import run as orun
+
+F32 = np.float32
+
+
+def f16_ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """ulp distance between fp16 bit patterns (ordered-integer mapping)."""
+    def ordered(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x8000, 0x8000 - (x & 0x7FFF), 0x8000 + x)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def max_rel_err(got: np.ndarray, want: np.ndarray) -> float:
+    g = got.astype(np.float64)
+    w = want.astype(np.float64)
+    zero = w == 0
+    if np.any(g[zero] != 0):
+        return float("inf")
+    nz = ~zero
+    if not nz.any():
+        return 0.0
+    return float(np.max(np.abs(g[nz] - w[nz]) / np.abs(w[nz])))
+
+
+@dataclass
+class StepReport:
+    step: int
+    skip: bool
+    coef: float
+    mismatches: dict = field(default_factory=dict)
+    max_rel: dict = field(default_factory=dict)
+
+
+def compare_state(rep: StepReport, name: str, got: np.ndarray, want: np.ndarray):
+    if name == "slot":
+        d = f16_ulp_diff(got, want.view(np.uint16) if want.dtype != np.uint16 else want)
+        rep.max_rel[name] = float(d.max()) if d.size else 0.0
+        rep.mismatches[name] = int(np.count_nonzero(d))
+        assert rep.max_rel[name] <= 1, (rep.step, name, rep.max_rel[name])
+    else:
+        rep.max_rel[name] = max_rel_err(got, want)
+        rep.mismatches[name] = int(np.count_nonzero(got.view(np.uint32) != want.view(np.uint32)))
+        assert rep.max_rel[name] <= 1e-6, (rep.step, name, rep.max_rel[name])
+
+
+def check_result(res, fin: oracle.FinalizeResult, step: int):
+    assert res.own_q == fin.own_q, (step, res.own_q, fin.own_q)
+    assert res.own_sq == fin.own_sq, (step, res.own_sq, fin.own_sq)
+    assert res.total_sq == fin.total_sq, (step, res.total_sq, fin.total_sq)
+    assert res.norm == fin.norm, (step, res.norm, fin.norm)
+    assert np.float32(res.clip_coef) == fin.coef, (step, res.clip_coef, fin.coef)
+    assert bool(res.overflow) == fin.overflow and bool(res.skip) == fin.skip, step
+
+
+def other_overflow_at(w: synth.Workload, step: int, flat_begin: int, count: int) -> bool:
+    """True if the workload's injected inf at `step` lies outside this window
+    (so another rank, not this one, reports the overflow)."""
+    site = synth.inject_site(w, step)
+    if site is None:
+        return False
+    return not (flat_begin <= site[1] < flat_begin + count)
+
+
+def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Optional[int] = None,
+               fused: bool = True, strict: bool = True) -> List[StepReport]:
+    """Run `steps` steps of the workload on one window of rank's shard on the
+    GPU and in the oracle; compare every step."""
+    import zero_sharded_optimizer_rank_amd.abi as abi
+    from zero_sharded_optimizer_rank_amd.shard import DeviceShard
+
+    steps = w.steps if steps is None else steps
+    dev = DeviceShard(w, rank, begin, count)
+    dev.load_initial_state()
+    p = orun.workload_plan(w)
+    flat_begin = rank * p.shard + begin
+    assert flat_begin == dev.flat_begin
+    op, om, ov, oh = orun.initial_state(w, p, rank, begin, count)
+    oh = oh.view(np.uint16)
+    other_sq = w.other_sq(p.real(rank)) if w.other_ranks_from_config else 0.0
+    scaler = abi.new_scaler(w.loss_scale0)
+    o_scale, o_good, o_t = w.loss_scale0, 0, 0
+    reports = []
+    for step in range(1, steps + 1):
+        assert scaler.scale == o_scale
+        ovf_other = other_overflow_at(w, step, flat_begin, count)
+        # GPU
+        dev.load_contributions(step, scaler.scale)
+        args = dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq, other_overflow=ovf_other)
+        if fused:
+            dev.step(args)
+        else:
+            dev.reduce_check(args)
+            dev.adam_apply(args)
+        res = dev.result()
+        # oracle
+        c = orun.shard_contrib(w, p, rank, step, o_scale, begin, count)
+        sc = oracle.step_scalars(w.lr, w.betas[0], w.betas[1], w.eps, w.weight_decay, o_t + 1,
+                                 w.world_size, o_scale)
+        out = oracle.shard_step(c, op, om, ov, oh, sc, w.max_grad_norm, other_sq=other_sq,
+                                other_overflow=ovf_other)
+        check_result(res, out.fin, step)
+        rep = StepReport(step, out.fin.skip, float(out.fin.coef))
+        g = dev.fetch("grad")
+        rep.mismatches["grad"] = int(np.count_nonzero(g.view(np.uint32) != out.g.view(np.uint32)))
+        assert rep.mismatches["grad"] == 0, (step, "grad")
+        op, om, ov = out.p, out.m, out.v
+        oh = out.h.view(np.uint16)
+        for name, want in (("master", op), ("m", om), ("v", ov), ("slot", oh)):
+            compare_state(rep, name, dev.fetch(name), want)
+        if strict:
+            assert all(v == 0 for v in rep.mismatches.values()), (step, rep.mismatches)
+        assert dev.guards_intact(), step
+        reports.append(rep)
+        abi.zero_scaler_update(scaler, bool(res.skip))
+        o_scale, o_good = oracle.scaler_update(o_scale, o_good, out.fin.skip)
+        if not out.fin.skip:
+            o_t += 1
+        assert scaler.t == o_t
+    return reports

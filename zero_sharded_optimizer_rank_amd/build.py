@@ -1,0 +1,62 @@
+"""Build libzero_shard.so for gfx950 in-tree with hipcc.
+
+Floating-point flags matter for results: no contraction into FMA, correctly
+rounded fp32 division and square root, denormals kept, and no packed fp32
+instructions.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libzero_shard.so")
+CALIB_LIB = os.path.join(HERE, "libzero_calib.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FP_FLAGS = [
+    "-ffp-contract=off",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-fno-gpu-flush-denormals-to-zero",
+]
+DEVICE_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-I", INCLUDE, "-I", CSRC]
+
+
+def _run(cmd):
+    print("+", " ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    kobj = os.path.join(BUILD_DIR, "zero_kernels.o")
+    hobj = os.path.join(BUILD_DIR, "zero_host.o")
+    _run([HIPCC, "-x", "hip", *COMMON, *FP_FLAGS, *DEVICE_FLAGS, "-c",
+          os.path.join(CSRC, "zero_kernels.hip"), "-o", kobj])
+    _run([HIPCC, *COMMON, "-ffp-contract=off", "-c", os.path.join(CSRC, "zero_host.cpp"),
+          "-o", hobj])
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, hobj, "-o", tmp])
+    os.replace(tmp, LIB)
+    # measurement-only copy kernel, in a library of its own
+    tmp = CALIB_LIB + ".tmp"
+    _run([HIPCC, "-x", "hip", *COMMON, *DEVICE_FLAGS, "-shared",
+          os.path.join(CSRC, "calib.hip"), "-o", tmp])
+    os.replace(tmp, CALIB_LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

@@ -1,0 +1,42 @@
+// Internal interface between the host-side C ABI (zero_host.cpp) and the
+// device kernels with their launchers (zero_kernels.hip).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "zero_shard.h"
+
+namespace zk {
+
+constexpr int kThreads = 256;        // threads per workgroup (four 64-wide waves)
+constexpr int kMaxBlocks = 8192;     // cap on workgroups of the reduce kernel
+constexpr size_t kTicketBytes = 256; // ticket word, padded to keep partials aligned
+constexpr size_t kPartialBytes = 32;
+constexpr size_t kWorkspaceBytes = kTicketBytes + (size_t)kMaxBlocks * kPartialBytes;
+
+// fp64 inputs of the norm / clip / skip decision.
+struct FinalizeArgs {
+  double inv64;     // 1 / (N * loss_scale)
+  double max_norm;  // <= 0: no clipping
+  double other_sq;  // fp64 stand-in for the other ranks' squared norm
+  uint64_t other_lo, other_hi;
+  int32_t other_overflow;
+  int32_t pad;
+};
+
+// fp32 Adam coefficients, each rounded once from fp64 on the host.
+struct AdamScalars {
+  float b1, omb1, b2, omb2, eps, step_size, sqrt_bc2, decay;
+};
+
+// Launchers: arguments already validated.  Return hipSuccess or the error.
+int launch_reduce_check(const uint16_t* const* contrib, int n, int64_t shard, float inv32,
+                        float* grad, void* workspace, const FinalizeArgs& fa,
+                        zero_step_result_t* res, hipStream_t stream);
+int launch_finalize(const FinalizeArgs& fa, zero_step_result_t* res, hipStream_t stream);
+int launch_adam(const float* grad, float* master, float* m, float* v, uint16_t* slot,
+                int64_t shard, const AdamScalars& sc, const zero_step_result_t* res,
+                hipStream_t stream);
+
+}  // namespace zk

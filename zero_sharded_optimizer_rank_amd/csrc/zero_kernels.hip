@@ -1,0 +1,388 @@
+// Device kernels of the ZeRO shard step for CDNA4 (gfx950).
+//
+// K1 (reduce_check): the reduce side of the gradient reduce-scatter, done in
+//   HBM ("10.6 ZeRO 与 FSDP", §10.6.1 and §10.6.2 step 2): for each element of
+//   the shard, the N fp16 contributions are summed in rank order 0..N-1 into
+//   an fp32 accumulator that starts at +0, then scaled by inv = 1/(N*loss
+//   scale) and written as the fp32 gradient.  Alongside, each thread keeps an
+//   overflow flag and the exact sum of acc^2 as a 128-bit integer.  Block
+//   partials go to the workspace; the last block to finish (ticket counter)
+//   sums them and makes the clip / skip decision.
+// K2 (adam): mixed-precision AdamW on the shard and the fp16 cast into the
+//   all-gather slot (§10.6.2 steps 3 and 4), skipped as a whole on overflow.
+//
+// Both kernels stream: every element is touched once, in 8-element groups
+// (one 16-byte load per fp16 contribution row, two per fp32 array), so a
+// 64-wide wave moves 1 KiB per fp16 row and 2 KiB per fp32 array per
+// instruction.  Nothing is a dense contraction, so no matrix cores are used;
+// HBM bandwidth bounds both kernels.
+//
+// Floating point: every fp32 operation is rounded on its own (contraction is
+// off here and in the build flags); division and square root are correctly
+// rounded; denormals are kept.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zero_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace zk {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct ContribTable {
+  const uint16_t* p[ZERO_MAX_RANKS];
+};
+
+struct Partial {
+  uint64_t lo, hi;
+  uint32_t bad;
+  uint32_t pad[3];
+};
+static_assert(sizeof(Partial) == kPartialBytes, "partial layout");
+
+__device__ __forceinline__ float h2f(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+__device__ __forceinline__ uint32_t f2h(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// acc^2 in units of 2^-48 as a 128-bit integer (lo, hi); sets bad for a
+// non-finite acc, which contributes nothing.  With m the 24-bit significand
+// and e the biased exponent, acc^2 = m^2 * 2^(2e - 300) = m^2 * 2^(2e - 252)
+// units.  Sums of fp16 values are multiples of 2^-24, so a right shift here
+// only drops zero bits.
+__device__ __forceinline__ void sq_units(float acc, uint64_t& lo, uint64_t& hi, uint32_t& bad) {
+  const uint32_t bits = __float_as_uint(acc) & 0x7FFFFFFFu;
+  const uint32_t e = bits >> 23;
+  const bool fin = e != 0xFFu;
+  bad |= fin ? 0u : 1u;
+  uint32_t mant = (bits & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+  mant = fin ? mant : 0u;
+  const int sh = 2 * (int)(e ? e : 1u) - 252;
+  const uint64_t sq = (uint64_t)mant * (uint64_t)mant;  // < 2^48
+  const uint32_t s = (uint32_t)(sh < 0 ? -sh : sh);
+  const uint64_t l_lo = s < 64 ? (sq << (s & 63)) : 0ull;
+  const uint64_t l_hi = s == 0 ? 0ull
+                        : s < 64 ? (sq >> ((64 - s) & 63))
+                        : s < 128 ? (sq << ((s - 64) & 63))
+                        : 0ull;
+  const uint64_t r_lo = s < 64 ? (sq >> (s & 63)) : 0ull;
+  lo = sh >= 0 ? l_lo : r_lo;
+  hi = sh >= 0 ? l_hi : 0ull;
+}
+
+__device__ __forceinline__ void add128(uint64_t& alo, uint64_t& ahi, uint64_t blo, uint64_t bhi) {
+  alo += blo;
+  ahi += bhi + (alo < blo ? 1ull : 0ull);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int mask) {
+  return (uint64_t)__shfl_xor((long long)x, mask);
+}
+
+// Sum (lo, hi, bad) over the workgroup; the result is valid in thread 0.
+__device__ void block_reduce(uint64_t& lo, uint64_t& hi, uint32_t& bad) {
+  __shared__ uint64_t s_lo[kThreads / 64], s_hi[kThreads / 64];
+  __shared__ uint32_t s_bad[kThreads / 64];
+  for (int off = 32; off > 0; off >>= 1) {
+    add128(lo, hi, shfl_xor_u64(lo, off), shfl_xor_u64(hi, off));
+    bad |= (uint32_t)__shfl_xor((int)bad, off);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_lo[wave] = lo;
+    s_hi[wave] = hi;
+    s_bad[wave] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kThreads / 64; ++w) {
+      add128(lo, hi, s_lo[w], s_hi[w]);
+      bad |= s_bad[w];
+    }
+  }
+}
+
+// Round a nonnegative integer c*2^128 + hi*2^64 + lo (c in {0,1}) to the
+// nearest fp64, ties to even.
+__device__ double u129_to_f64(uint32_t c, uint64_t hi, uint64_t lo) {
+  if (!c && !hi) return (double)lo;  // uint64 -> fp64 rounds once
+  uint64_t top, scale_exp;
+  bool sticky;
+  if (c) {
+    top = 0x8000000000000000ull | (hi >> 1);
+    sticky = (hi & 1ull) || lo;
+    scale_exp = 65;
+  } else {
+    const int lz = __clzll((long long)hi);
+    top = lz ? ((hi << lz) | (lo >> (64 - lz))) : hi;
+    sticky = (lz ? (lo << lz) : lo) != 0;
+    scale_exp = 64 - lz;
+  }
+  uint64_t keep = top >> 11;
+  const uint64_t rb = top & 0x7FFull;
+  if (rb > 0x400ull || (rb == 0x400ull && (sticky || (keep & 1ull)))) keep += 1;
+  return __builtin_ldexp((double)keep, (int)scale_exp + 11);
+}
+
+__device__ void finalize_into(uint64_t qlo, uint64_t qhi, uint32_t bad, const FinalizeArgs& fa,
+                              zero_step_result_t* res) {
+  // (qhi:qlo) + (other_hi:other_lo) as a 129-bit value (carry:thi:tlo)
+  const uint64_t tlo = qlo + fa.other_lo;
+  const uint64_t c0 = tlo < qlo ? 1ull : 0ull;
+  const uint64_t t1 = qhi + fa.other_hi;
+  const uint64_t thi = t1 + c0;
+  const uint32_t carry = ((t1 < qhi) || (thi < t1)) ? 1u : 0u;
+  const double own = ((u129_to_f64(0, qhi, qlo) * 0x1p-48) * fa.inv64) * fa.inv64;
+  const double tot = ((u129_to_f64(carry, thi, tlo) * 0x1p-48) * fa.inv64) * fa.inv64 + fa.other_sq;
+  const double norm = __builtin_sqrt(tot);
+  double coef = 1.0;
+  if (fa.max_norm > 0.0) {
+    const double c = fa.max_norm / (norm + 1e-6);
+    coef = (c < 1.0) ? c : 1.0;
+  }
+  res->own_q_lo = qlo;
+  res->own_q_hi = qhi;
+  res->own_sq = own;
+  res->total_sq = tot;
+  res->norm = norm;
+  res->clip_coef = (float)coef;
+  res->overflow = bad ? 1 : 0;
+  res->skip = (bad || fa.other_overflow || carry) ? 1 : 0;
+  res->reserved = 0;
+}
+
+// ---------------------------------------------------------------------------
+// K1: reduce, unscale, overflow flag, exact squared norm; last block finalizes.
+constexpr int kRankBatch = 8;  // contribution rows loaded before they are summed
+
+__global__ __launch_bounds__(kThreads) void k1_reduce_check(
+    ContribTable ct, int32_t n, int64_t shard, float inv32, float* __restrict__ grad,
+    Partial* __restrict__ partials, uint32_t* __restrict__ ticket, FinalizeArgs fa,
+    zero_step_result_t* __restrict__ res) {
+  const int64_t full = shard >> 3;
+  const int64_t total = (shard + 7) >> 3;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  uint64_t qlo = 0, qhi = 0;
+  uint32_t bad = 0;
+  for (int64_t grp = (int64_t)blockIdx.x * kThreads + threadIdx.x; grp < total; grp += stride) {
+    if (grp < full) {
+      const int64_t off = grp * 8;
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+      for (int r0 = 0; r0 < n; r0 += kRankBatch) {
+        u32x4 d[kRankBatch];
+#pragma unroll
+        for (int b = 0; b < kRankBatch; ++b)
+          if (r0 + b < n)
+            d[b] = __builtin_nontemporal_load((const u32x4*)(ct.p[r0 + b] + off));
+#pragma unroll
+        for (int b = 0; b < kRankBatch; ++b) {
+          if (r0 + b < n) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              acc[2 * w] = acc[2 * w] + h2f(d[b][w] & 0xFFFFu);
+              acc[2 * w + 1] = acc[2 * w + 1] + h2f(d[b][w] >> 16);
+            }
+          }
+        }
+      }
+      f32x4 g0, g1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        g0[e] = acc[e] * inv32;
+        g1[e] = acc[4 + e] * inv32;
+      }
+      __builtin_nontemporal_store(g0, (f32x4*)(grad + off));
+      __builtin_nontemporal_store(g1, (f32x4*)(grad + off + 4));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint64_t lo, hi;
+        sq_units(acc[e], lo, hi, bad);
+        add128(qlo, qhi, lo, hi);
+      }
+    } else {
+      // ragged tail: the last shard % 8 elements
+      for (int64_t j = grp * 8; j < shard; ++j) {
+        float a = 0.0f;
+        for (int r = 0; r < n; ++r) a = a + h2f(ct.p[r][j]);
+        grad[j] = a * inv32;
+        uint64_t lo, hi;
+        sq_units(a, lo, hi, bad);
+        add128(qlo, qhi, lo, hi);
+      }
+    }
+  }
+
+  block_reduce(qlo, qhi, bad);
+  __shared__ uint32_t s_last;
+  if (threadIdx.x == 0) {
+    Partial pt;
+    pt.lo = qlo;
+    pt.hi = qhi;
+    pt.bad = bad;
+    pt.pad[0] = pt.pad[1] = pt.pad[2] = 0;
+    partials[blockIdx.x] = pt;
+    __threadfence();
+    const uint32_t prev = atomicAdd(ticket, 1u);
+    s_last = (prev == gridDim.x - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  uint64_t tlo = 0, thi = 0;
+  uint32_t tbad = 0;
+  for (uint32_t i = threadIdx.x; i < gridDim.x; i += kThreads) {
+    const Partial pt = partials[i];
+    add128(tlo, thi, pt.lo, pt.hi);
+    tbad |= pt.bad;
+  }
+  block_reduce(tlo, thi, tbad);
+  if (threadIdx.x == 0) {
+    finalize_into(tlo, thi, tbad, fa, res);
+    *ticket = 0u;  // ready for the next call
+  }
+}
+
+__global__ void k_finalize(FinalizeArgs fa, zero_step_result_t* res) {
+  if (threadIdx.x == 0 && blockIdx.x == 0)
+    finalize_into(res->own_q_lo, res->own_q_hi, (uint32_t)res->overflow, fa, res);
+}
+
+// ---------------------------------------------------------------------------
+// K2: AdamW on the shard and the fp16 cast into the slot.
+__device__ __forceinline__ void adam1(float g, float c, const AdamScalars& sc, float& p, float& m,
+                                      float& v) {
+  const float gc = g * c;
+  m = sc.b1 * m + sc.omb1 * gc;
+  v = sc.b2 * v + sc.omb2 * (gc * gc);
+  const float den = __builtin_sqrtf(v) / sc.sqrt_bc2 + sc.eps;
+  const float u = (m / den) * sc.step_size;
+  p = p * sc.decay - u;
+}
+
+__global__ __launch_bounds__(kThreads) void k2_adam(
+    const float* __restrict__ grad, float* __restrict__ master, float* __restrict__ mom,
+    float* __restrict__ var, uint16_t* __restrict__ slot, int64_t shard, AdamScalars sc,
+    const zero_step_result_t* __restrict__ res) {
+  if (res->skip) return;
+  const float c = res->clip_coef;
+  const bool slot_aligned = (((uintptr_t)slot) & 15u) == 0;
+  const int64_t full = shard >> 3;
+  const int64_t total = (shard + 7) >> 3;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t grp = (int64_t)blockIdx.x * kThreads + threadIdx.x; grp < total; grp += stride) {
+    if (grp < full) {
+      const int64_t off = grp * 8;
+      f32x4 g[2], p[2], m[2], v[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        g[h] = __builtin_nontemporal_load((const f32x4*)(grad + off + 4 * h));
+        p[h] = __builtin_nontemporal_load((const f32x4*)(master + off + 4 * h));
+        m[h] = __builtin_nontemporal_load((const f32x4*)(mom + off + 4 * h));
+        v[h] = __builtin_nontemporal_load((const f32x4*)(var + off + 4 * h));
+      }
+      uint32_t hb[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pp = p[h][e], mm = m[h][e], vv = v[h][e];
+          adam1(g[h][e], c, sc, pp, mm, vv);
+          p[h][e] = pp;
+          m[h][e] = mm;
+          v[h][e] = vv;
+          hb[4 * h + e] = f2h(pp);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        __builtin_nontemporal_store(p[h], (f32x4*)(master + off + 4 * h));
+        __builtin_nontemporal_store(m[h], (f32x4*)(mom + off + 4 * h));
+        __builtin_nontemporal_store(v[h], (f32x4*)(var + off + 4 * h));
+      }
+      if (slot_aligned) {
+        u32x4 o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) o[w] = hb[2 * w] | (hb[2 * w + 1] << 16);
+        __builtin_nontemporal_store(o, (u32x4*)(slot + off));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) slot[off + e] = (uint16_t)hb[e];
+      }
+    } else {
+      for (int64_t j = grp * 8; j < shard; ++j) {
+        float pp = master[j], mm = mom[j], vv = var[j];
+        adam1(grad[j], c, sc, pp, mm, vv);
+        master[j] = pp;
+        mom[j] = mm;
+        var[j] = vv;
+        slot[j] = (uint16_t)f2h(pp);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+int g_cu_count[64];
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && g_cu_count[dev] > 0) return g_cu_count[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (dev < 64) g_cu_count[dev] = cus;
+  return cus;
+}
+
+// Workgroups for a streaming pass over `groups` 8-element groups: enough for
+// eight resident workgroups per CU, never more than there are groups.
+int stream_blocks(int64_t groups, int per_cu) {
+  int64_t want = (groups + kThreads - 1) / kThreads;
+  int64_t cap = (int64_t)cu_count() * per_cu;
+  if (cap > kMaxBlocks) cap = kMaxBlocks;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  return (int)want;
+}
+
+}  // namespace
+
+int launch_reduce_check(const uint16_t* const* contrib, int n, int64_t shard, float inv32,
+                        float* grad, void* workspace, const FinalizeArgs& fa,
+                        zero_step_result_t* res, hipStream_t stream) {
+  ContribTable ct;
+  for (int r = 0; r < ZERO_MAX_RANKS; ++r) ct.p[r] = r < n ? contrib[r] : nullptr;
+  uint32_t* ticket = (uint32_t*)workspace;
+  Partial* partials = (Partial*)((char*)workspace + kTicketBytes);
+  const int blocks = stream_blocks((shard + 7) >> 3, 8);
+  hipLaunchKernelGGL(k1_reduce_check, dim3(blocks), dim3(kThreads), 0, stream, ct, n, shard, inv32,
+                     grad, partials, ticket, fa, res);
+  return (int)hipGetLastError();
+}
+
+int launch_finalize(const FinalizeArgs& fa, zero_step_result_t* res, hipStream_t stream) {
+  hipLaunchKernelGGL(k_finalize, dim3(1), dim3(64), 0, stream, fa, res);
+  return (int)hipGetLastError();
+}
+
+int launch_adam(const float* grad, float* master, float* m, float* v, uint16_t* slot,
+                int64_t shard, const AdamScalars& sc, const zero_step_result_t* res,
+                hipStream_t stream) {
+  const int blocks = stream_blocks((shard + 7) >> 3, 8);
+  hipLaunchKernelGGL(k2_adam, dim3(blocks), dim3(kThreads), 0, stream, grad, master, m, v, slot,
+                     shard, sc, res);
+  return (int)hipGetLastError();
+}
+
+}  // namespace zk

@@ -1,0 +1,177 @@
+"""One rank's shard on one GPU: device buffers, seeded input feeding, step calls.
+
+PyTorch supplies device memory, pinned host memory and the stream; the work of
+the step runs in libzero_shard.so through ``abi``.  Inputs come from the
+seeded generator in ``synth`` (host, pinned staging, async copies).
+
+A ``DeviceShard`` can hold a window [begin, begin+count) of the rank's shard
+instead of the whole shard: the kernels then treat the window as the shard,
+which is how parity runs at sizes the oracle finishes quickly.  The fp16 slot
+keeps the misalignment it has in the real flat buffer (flat16 + rank*S +
+begin), and guard words on either side catch stray writes.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+import torch
+
+import synth
+
+from . import abi
+
+GUARD = 64  # fp16 guard elements on each side of the slot
+GUARD_WORD = 0x5A5A
+CHUNK = 1 << 25  # elements per host staging chunk
+
+
+def round_up(x: int, a: int) -> int:
+    return (x + a - 1) // a * a
+
+
+class DeviceShard:
+    def __init__(self, w: synth.Workload, rank: int, begin: int = 0, count: Optional[int] = None,
+                 device: str = "cuda:0", stream: Optional[torch.cuda.Stream] = None):
+        self.w = w
+        self.rank = rank
+        self.device = torch.device(device)
+        full_plan, self.offsets = abi.zero_plan(w.numels, w.world_size)
+        self.full_plan = full_plan
+        s_full = full_plan.shard
+        if count is None:
+            count = s_full - begin
+        if not (0 <= begin and begin + count <= s_full):
+            raise ValueError("window outside the shard")
+        self.begin, self.count = begin, count
+        self.flat_begin = rank * s_full + begin  # flat index of the window's first element
+        real = max(0, min(count, w.psi - self.flat_begin))
+        n = w.world_size
+        self.plan = abi.zero_plan_t(real, n, 1, count, count * n)
+        self.stream = stream or torch.cuda.current_stream(self.device)
+        ld = round_up(max(count, 1), 8)
+        self.ld = ld
+        self.contrib = torch.empty((n, ld), dtype=torch.int16, device=self.device)
+        self.master = torch.empty(max(count, 1), dtype=torch.float32, device=self.device)
+        self.m = torch.zeros_like(self.master)
+        self.v = torch.zeros_like(self.master)
+        self.grad = torch.empty_like(self.master)
+        # slot with the real buffer's alignment (flat_begin mod 8) plus guards
+        self.mis = self.flat_begin % 8
+        self.slot_buf = torch.full((GUARD + 8 + count + GUARD,), GUARD_WORD, dtype=torch.int16,
+                                   device=self.device)
+        self.slot_off = GUARD + self.mis
+        self.ws = torch.zeros(abi.zero_workspace_bytes(), dtype=torch.uint8, device=self.device)
+        self.res = torch.zeros(abi.RESULT_BYTES, dtype=torch.uint8, device=self.device)
+        chunk = min(CHUNK, max(count, 1))
+        self._pin16 = [torch.empty(chunk, dtype=torch.int16, pin_memory=True) for _ in range(2)]
+        self._pin32 = torch.empty(chunk, dtype=torch.float32, pin_memory=True)
+        self._chunk = chunk
+        self._ev = [torch.cuda.Event() for _ in range(2)]
+
+    # ------------------------------------------------------------------ views
+    @property
+    def slot(self) -> torch.Tensor:
+        return self.slot_buf[self.slot_off:self.slot_off + self.count]
+
+    def slot_ptr(self) -> int:
+        return self.slot_buf.data_ptr() + 2 * self.slot_off
+
+    def contrib_ptrs(self):
+        base = self.contrib.data_ptr()
+        return [base + 2 * self.ld * r for r in range(self.w.world_size)]
+
+    def guards_intact(self) -> bool:
+        b = self.slot_buf
+        lo = b[:self.slot_off]
+        hi = b[self.slot_off + self.count:]
+        return bool((lo == GUARD_WORD).all().item()) and bool((hi == GUARD_WORD).all().item())
+
+    # ---------------------------------------------------------------- feeding
+    def _feed16(self, row: torch.Tensor, fill):
+        """Fill a device int16 row of self.count elements chunk by chunk."""
+        with torch.cuda.stream(self.stream):
+            for i, s in enumerate(range(0, self.count, self._chunk)):
+                k = min(self._chunk, self.count - s)
+                buf = self._pin16[i % 2]
+                self._ev[i % 2].synchronize()
+                fill(s, k, buf.numpy()[:k].view(np.uint16))
+                row[s:s + k].copy_(buf[:k], non_blocking=True)
+                self._ev[i % 2].record(self.stream)
+        self.stream.synchronize()
+
+    def load_contributions(self, step: int, loss_scale: float):
+        """Rank q's row: the window of rank q's scaled fp16 gradient at `step`."""
+        for q in range(self.w.world_size):
+            def fill(s, k, out, q=q):
+                synth.contributions(self.w, step, q, self.flat_begin + s, k, loss_scale, out=out)
+            self._feed16(self.contrib[q], fill)
+
+    def load_initial_state(self):
+        """Seeded fp32 masters, m = v = 0, and the slot = fp16(master)."""
+        with torch.cuda.stream(self.stream):
+            for s in range(0, self.count, self._chunk):
+                k = min(self._chunk, self.count - s)
+                synth.masters(self.w, self.flat_begin + s, k, out=self._pin32.numpy()[:k])
+                self.master[s:s + k].copy_(self._pin32[:k], non_blocking=True)
+                self.stream.synchronize()
+            self.m.zero_()
+            self.v.zero_()
+            self.slot.copy_(self.master[:self.count].to(torch.float16).view(torch.int16))
+        self.stream.synchronize()
+
+    # ------------------------------------------------------------------ steps
+    def args(self, step_t: int, loss_scale: float, max_norm: Optional[float] = None,
+             other_sq: float = 0.0, other_q: int = 0, other_overflow: bool = False):
+        w = self.w
+        return abi.step_args(lr=w.lr, beta1=w.betas[0], beta2=w.betas[1], eps=w.eps,
+                             weight_decay=w.weight_decay,
+                             max_grad_norm=w.max_grad_norm if max_norm is None else max_norm,
+                             loss_scale=loss_scale, step=step_t, other_sq=other_sq,
+                             other_q=other_q, other_overflow=other_overflow)
+
+    def reduce_check(self, args):
+        abi.zero_reduce_check(self.plan, self.rank_in_plan, self.contrib_ptrs(), args, self.grad,
+                              self.ws, self.ws.numel(), self.res, self.stream)
+
+    def finalize(self, args):
+        abi.zero_finalize(self.plan, args, self.res, self.stream)
+
+    def adam_apply(self, args):
+        abi.zero_adam_apply(self.plan, self.rank_in_plan, self.grad, self.master, self.m, self.v,
+                            self.slot_ptr(), args, self.res, self.stream)
+
+    def step(self, args):
+        abi.zero_reduce_adam_step(self.plan, self.rank_in_plan, self.contrib_ptrs(), self.master,
+                                  self.m, self.v, self.slot_ptr(), self.grad, self.ws,
+                                  self.ws.numel(), args, self.res, self.stream)
+
+    @property
+    def rank_in_plan(self) -> int:
+        return self.rank
+
+    def result(self) -> abi.zero_step_result_t:
+        self.stream.synchronize()
+        raw = self.res.cpu().numpy().tobytes()
+        return abi.zero_step_result_t.from_buffer_copy(raw)
+
+    def fetch(self, name: str, idx=None) -> np.ndarray:
+        """Copy a state array (or selected indexes of it) back to the host."""
+        self.stream.synchronize()
+        t = {"grad": self.grad, "master": self.master, "m": self.m, "v": self.v}.get(name)
+        if name == "slot":
+            t = self.slot
+        else:
+            t = t[:self.count]
+        if idx is not None:
+            t = t[torch.as_tensor(idx, device=self.device)]
+        a = t.cpu().numpy()
+        return a.view(np.uint16) if name == "slot" else a
+
+
+def result_from_bytes(b: bytes) -> abi.zero_step_result_t:
+    return abi.zero_step_result_t.from_buffer_copy(b)
+
+
+__all__ = ["DeviceShard", "round_up", "result_from_bytes", "ctypes"]
