@@ -160,10 +160,11 @@ typedef struct zero_step_result {
   int32_t reserved;
 } zero_step_result_t;
 
-/* Bytes of workspace zero_reduce_check needs (fixed; 256 KiB + 256).  The
- * workspace must be zero-filled before its first use; every call leaves it
- * ready for the next. */
-size_t zero_workspace_bytes(void);
+/* Bytes of workspace zero_reduce_check needs for plan->shard elements:
+ * 256 + 16 * (256 + ceil(ceil(S / 8) / 256)), about S / 128 bytes; 0 for a
+ * NULL plan or a shard outside 0..ZERO_MAX_SHARD.  The workspace must be
+ * zero-filled before its first use; every call leaves it ready for the next. */
+size_t zero_workspace_bytes(const zero_plan_t* plan);
 
 /*
  * zero_reduce_check: step 1 and 2 for rank's shard of S = plan->shard elements.

@@ -100,5 +100,9 @@ def test_host_argument_errors():
     with pytest.raises(abi.ZeroError):
         abi.zero_plan_segments(plan, [10, 10, 10], offs, 3)
     assert abi.zero_plan_real(plan, 5) == -1
-    assert abi.zero_workspace_bytes() == 256 + 8192 * 32
+    for shard in (0, 1, 8, 2048, 2049, 10**9):
+        p = abi.zero_plan_t(shard, 1, 1, shard, shard)
+        groups = -(-shard // 8)
+        assert abi.zero_workspace_bytes(p) == 256 + 16 * (256 + max(1, -(-groups // 256)))
+    assert abi.zero_workspace_bytes(abi.zero_plan_t(0, 1, 1, -1, -1)) == 0
     assert abi.RESULT_BYTES == 56

@@ -229,7 +229,7 @@ def test_empty_shard():
     abi = _abi()
     n = 4
     plan = abi.zero_plan_t(0, n, 1, 0, 0)
-    ws = torch.zeros(abi.zero_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(abi.zero_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
     res = torch.zeros(abi.RESULT_BYTES, dtype=torch.uint8, device="cuda")
     dummy = torch.zeros(16, dtype=torch.float32, device="cuda")
     args = abi.step_args(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
@@ -244,7 +244,7 @@ def test_empty_shard():
 def test_argument_errors():
     abi = _abi()
     plan, _ = abi.zero_plan([1000], 4)
-    ws = torch.zeros(abi.zero_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(abi.zero_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
     res = torch.zeros(abi.RESULT_BYTES, dtype=torch.uint8, device="cuda")
     buf = torch.zeros(4096, dtype=torch.float32, device="cuda")
     good = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, max_grad_norm=1.0,

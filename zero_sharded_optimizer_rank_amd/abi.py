@@ -14,7 +14,7 @@ import os
 from typing import Sequence, Tuple
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libzero_shard.so")
+LIB_PATH = os.environ.get("ZERO_SHARD_LIB") or os.path.join(HERE, "libzero_shard.so")
 
 ZERO_OK, ZERO_EINVAL, ZERO_EALIGN, ZERO_ENOSPC, ZERO_EHIP = 0, -1, -2, -3, -4
 ZERO_MAX_RANKS = 64
@@ -81,7 +81,7 @@ _SIGNATURES = {
                                           ctypes.c_int32, _P(ctypes.c_int32)]),
     "zero_state_bytes": (ctypes.c_double, [ctypes.c_int32, ctypes.c_double, ctypes.c_double,
                                            ctypes.c_double]),
-    "zero_workspace_bytes": (ctypes.c_size_t, []),
+    "zero_workspace_bytes": (ctypes.c_size_t, [_P(zero_plan_t)]),
     "zero_reduce_check": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _P(_vp),
                                          _P(zero_step_args_t), _vp, _vp, ctypes.c_size_t, _vp,
                                          _vp]),
@@ -168,8 +168,8 @@ def zero_state_bytes(stage: int, psi: float, n: float, k: float = 12.0) -> float
     return float(lib().zero_state_bytes(stage, psi, n, k))
 
 
-def zero_workspace_bytes() -> int:
-    return int(lib().zero_workspace_bytes())
+def zero_workspace_bytes(plan: zero_plan_t) -> int:
+    return int(lib().zero_workspace_bytes(ctypes.byref(plan)))
 
 
 def step_args(*, lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,

@@ -101,8 +101,8 @@ int check_reduce_ptrs(const zero_plan_t* plan, const uint16_t* const* contrib, f
   if (!aligned(dev_result, 8)) return fail(ZERO_EALIGN, "dev_result not 8-byte aligned");
   if (!workspace) return fail(ZERO_EINVAL, "workspace is NULL");
   if (!aligned(workspace, 16)) return fail(ZERO_EALIGN, "workspace not 16-byte aligned");
-  if (ws_bytes < zk::kWorkspaceBytes)
-    return fail(ZERO_ENOSPC, "workspace %zu bytes < %zu", ws_bytes, zk::kWorkspaceBytes);
+  const size_t need = zk::workspace_bytes(plan->shard);
+  if (ws_bytes < need) return fail(ZERO_ENOSPC, "workspace %zu bytes < %zu", ws_bytes, need);
   if (plan->shard > 0) {
     if (!contrib) return fail(ZERO_EINVAL, "contrib is NULL");
     for (int64_t r = 0; r < plan->world_size; ++r) {
@@ -212,7 +212,10 @@ double zero_state_bytes(int32_t stage, double psi, double n, double k) {
   }
 }
 
-size_t zero_workspace_bytes(void) { return zk::kWorkspaceBytes; }
+size_t zero_workspace_bytes(const zero_plan_t* plan) {
+  if (!plan || plan->shard < 0 || plan->shard > ZERO_MAX_SHARD) return 0;
+  return zk::workspace_bytes(plan->shard);
+}
 
 int zero_reduce_check(const zero_plan_t* plan, int32_t rank, const uint16_t* const* contrib,
                       const zero_step_args_t* args, float* grad_out, void* workspace,

@@ -10,10 +10,9 @@
 namespace zk {
 
 constexpr int kThreads = 256;        // threads per workgroup (four 64-wide waves)
-constexpr int kMaxBlocks = 8192;     // cap on workgroups of the reduce kernel
+constexpr int kFinBlocks = 256;      // most workgroups of the partial-sum kernel
 constexpr size_t kTicketBytes = 256; // ticket word, padded to keep partials aligned
-constexpr size_t kPartialBytes = 32;
-constexpr size_t kWorkspaceBytes = kTicketBytes + (size_t)kMaxBlocks * kPartialBytes;
+constexpr size_t kPartialBytes = 16;
 
 // fp64 inputs of the norm / clip / skip decision.
 struct FinalizeArgs {
@@ -29,6 +28,11 @@ struct FinalizeArgs {
 struct AdamScalars {
   float b1, omb1, b2, omb2, eps, step_size, sqrt_bc2, decay;
 };
+
+// Workgroups of the reduce kernel for a shard, and the workspace it needs:
+// ticket, kFinBlocks second-level partials, one partial per workgroup.
+int64_t k1_blocks(int64_t shard);
+size_t workspace_bytes(int64_t shard);
 
 // Launchers: arguments already validated.  Return hipSuccess or the error.
 int launch_reduce_check(const uint16_t* const* contrib, int n, int64_t shard, float inv32,

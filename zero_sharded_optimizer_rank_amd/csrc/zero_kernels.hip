@@ -4,18 +4,21 @@
 //   HBM ("10.6 ZeRO 与 FSDP", §10.6.1 and §10.6.2 step 2): for each element of
 //   the shard, the N fp16 contributions are summed in rank order 0..N-1 into
 //   an fp32 accumulator that starts at +0, then scaled by inv = 1/(N*loss
-//   scale) and written as the fp32 gradient.  Alongside, each thread keeps an
-//   overflow flag and the exact sum of acc^2 as a 128-bit integer.  Block
-//   partials go to the workspace; the last block to finish (ticket counter)
-//   sums them and makes the clip / skip decision.
+//   scale) and written as the fp32 gradient.  Each thread also forms the
+//   overflow flag and the exact sum of acc^2 (a 128-bit integer); each
+//   workgroup writes one partial.
+// KF (finalize): sums the partials (integer sums, so any order gives the same
+//   bits), adds the other ranks' share and makes the clip / skip decision.
 // K2 (adam): mixed-precision AdamW on the shard and the fp16 cast into the
 //   all-gather slot (§10.6.2 steps 3 and 4), skipped as a whole on overflow.
 //
-// Both kernels stream: every element is touched once, in 8-element groups
-// (one 16-byte load per fp16 contribution row, two per fp32 array), so a
-// 64-wide wave moves 1 KiB per fp16 row and 2 KiB per fp32 array per
-// instruction.  Nothing is a dense contraction, so no matrix cores are used;
-// HBM bandwidth bounds both kernels.
+// K1 and K2 stream every element once and use one-shot grids: each thread
+// owns a fixed piece of the shard (no grid-stride loop), so workgroups are
+// dispatched in address order and retire as they finish; on MI355X this
+// streams measurably faster than persistent grids.  Loads and stores are 16
+// bytes per lane, so a 64-wide wave moves 1 KiB per instruction.  Nothing here
+// is a dense contraction, so no matrix cores are used; HBM bandwidth bounds
+// K1 and K2.
 //
 // Floating point: every fp32 operation is rounded on its own (contraction is
 // off here and in the build flags); division and square root are correctly
@@ -27,6 +30,26 @@
 
 #pragma clang fp contract(off)
 
+// Launch shape and cache hints (compile-time; measured on MI355X).
+#ifndef ZK_K1_GROUPS
+#define ZK_K1_GROUPS 1  // 8-element groups per K1 thread
+#endif
+#ifndef ZK_K2_QUADS
+#define ZK_K2_QUADS 2  // 4-element quads per K2 thread
+#endif
+#ifndef ZK_K1_NT_LOAD
+#define ZK_K1_NT_LOAD 1
+#endif
+#ifndef ZK_K1_NT_STORE
+#define ZK_K1_NT_STORE 1
+#endif
+#ifndef ZK_K2_NT_LOAD
+#define ZK_K2_NT_LOAD 1
+#endif
+#ifndef ZK_K2_NT_STORE
+#define ZK_K2_NT_STORE 1
+#endif
+
 namespace zk {
 namespace {
 
@@ -37,12 +60,27 @@ struct ContribTable {
   const uint16_t* p[ZERO_MAX_RANKS];
 };
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// A 128-bit partial sum; bit 63 of hi carries the overflow flag.
 struct Partial {
   uint64_t lo, hi;
-  uint32_t bad;
-  uint32_t pad[3];
 };
 static_assert(sizeof(Partial) == kPartialBytes, "partial layout");
+
+constexpr int kRankBatch = 8;  // contribution rows loaded before they are summed
+
+template <bool NT, typename T>
+__device__ __forceinline__ T load16(const T* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool NT, typename T>
+__device__ __forceinline__ void store16(T v, T* p) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
 
 __device__ __forceinline__ float h2f(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
@@ -159,56 +197,61 @@ __device__ void finalize_into(uint64_t qlo, uint64_t qhi, uint32_t bad, const Fi
 }
 
 // ---------------------------------------------------------------------------
-// K1: reduce, unscale, overflow flag, exact squared norm; last block finalizes.
-constexpr int kRankBatch = 8;  // contribution rows loaded before they are summed
-
-__global__ __launch_bounds__(kThreads) void k1_reduce_check(
-    ContribTable ct, int32_t n, int64_t shard, float inv32, float* __restrict__ grad,
-    Partial* __restrict__ partials, uint32_t* __restrict__ ticket, FinalizeArgs fa,
-    zero_step_result_t* __restrict__ res) {
-  const int64_t full = shard >> 3;
-  const int64_t total = (shard + 7) >> 3;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  uint64_t qlo = 0, qhi = 0;
-  uint32_t bad = 0;
-  for (int64_t grp = (int64_t)blockIdx.x * kThreads + threadIdx.x; grp < total; grp += stride) {
-    if (grp < full) {
-      const int64_t off = grp * 8;
-      float acc[8];
+// K1: reduce, unscale, overflow flag, exact squared norm, one partial per
+// workgroup.  Thread t of workgroup b owns groups b*256*G + u*256 + t,
+// u < G, so each load instruction of a wave covers 1 KiB of a row.
+__device__ __forceinline__ void reduce_group(const ContribTable& ct, int32_t n, int64_t grp,
+                                             float inv32, float* __restrict__ grad,
+                                             uint64_t& qlo, uint64_t& qhi, uint32_t& bad) {
+  const int64_t off = grp * 8;
+  float acc[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-      for (int r0 = 0; r0 < n; r0 += kRankBatch) {
-        u32x4 d[kRankBatch];
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int r0 = 0; r0 < n; r0 += kRankBatch) {
+    u32x4 d[kRankBatch];
 #pragma unroll
-        for (int b = 0; b < kRankBatch; ++b)
-          if (r0 + b < n)
-            d[b] = __builtin_nontemporal_load((const u32x4*)(ct.p[r0 + b] + off));
+    for (int b = 0; b < kRankBatch; ++b)
+      if (r0 + b < n) d[b] = load16<ZK_K1_NT_LOAD>((const u32x4*)(ct.p[r0 + b] + off));
 #pragma unroll
-        for (int b = 0; b < kRankBatch; ++b) {
-          if (r0 + b < n) {
+    for (int b = 0; b < kRankBatch; ++b) {
+      if (r0 + b < n) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              acc[2 * w] = acc[2 * w] + h2f(d[b][w] & 0xFFFFu);
-              acc[2 * w + 1] = acc[2 * w + 1] + h2f(d[b][w] >> 16);
-            }
-          }
+        for (int w = 0; w < 4; ++w) {
+          acc[2 * w] = acc[2 * w] + h2f(d[b][w] & 0xFFFFu);
+          acc[2 * w + 1] = acc[2 * w + 1] + h2f(d[b][w] >> 16);
         }
       }
-      f32x4 g0, g1;
+    }
+  }
+  f32x4 g0, g1;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        g0[e] = acc[e] * inv32;
-        g1[e] = acc[4 + e] * inv32;
-      }
-      __builtin_nontemporal_store(g0, (f32x4*)(grad + off));
-      __builtin_nontemporal_store(g1, (f32x4*)(grad + off + 4));
+  for (int e = 0; e < 4; ++e) {
+    g0[e] = acc[e] * inv32;
+    g1[e] = acc[4 + e] * inv32;
+  }
+  store16<ZK_K1_NT_STORE>(g0, (f32x4*)(grad + off));
+  store16<ZK_K1_NT_STORE>(g1, (f32x4*)(grad + off + 4));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint64_t lo, hi;
-        sq_units(acc[e], lo, hi, bad);
-        add128(qlo, qhi, lo, hi);
-      }
-    } else {
+  for (int e = 0; e < 8; ++e) {
+    uint64_t lo, hi;
+    sq_units(acc[e], lo, hi, bad);
+    add128(qlo, qhi, lo, hi);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k1_reduce_check(ContribTable ct, int32_t n,
+                                                            int64_t shard, float inv32,
+                                                            float* __restrict__ grad,
+                                                            Partial* __restrict__ partials) {
+  const int64_t full = shard >> 3;
+  uint64_t qlo = 0, qhi = 0;
+  uint32_t bad = 0;
+#pragma unroll
+  for (int u = 0; u < ZK_K1_GROUPS; ++u) {
+    const int64_t grp = ((int64_t)blockIdx.x * ZK_K1_GROUPS + u) * kThreads + threadIdx.x;
+    if (grp < full) {
+      reduce_group(ct, n, grp, inv32, grad, qlo, qhi, bad);
+    } else if (grp == full) {
       // ragged tail: the last shard % 8 elements
       for (int64_t j = grp * 8; j < shard; ++j) {
         float a = 0.0f;
@@ -220,16 +263,28 @@ __global__ __launch_bounds__(kThreads) void k1_reduce_check(
       }
     }
   }
-
   block_reduce(qlo, qhi, bad);
+  if (threadIdx.x == 0) partials[blockIdx.x] = Partial{qlo, qhi | ((uint64_t)(bad ? 1u : 0u) << 63)};
+}
+
+// ---------------------------------------------------------------------------
+// KF: sum the K1 partials, then the last workgroup finalizes.  A block
+// partial is below 2^105, so bit 63 of its high word is free for the flag.
+__global__ __launch_bounds__(kThreads) void kf_reduce_finalize(
+    const Partial* __restrict__ partials, int64_t n_partials, Partial* __restrict__ level2,
+    uint32_t* __restrict__ ticket, FinalizeArgs fa, zero_step_result_t* __restrict__ res) {
+  uint64_t lo = 0, hi = 0;
+  uint32_t bad = 0;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_partials;
+       i += (int64_t)gridDim.x * kThreads) {
+    const Partial pt = partials[i];
+    bad |= (uint32_t)(pt.hi >> 63);
+    add128(lo, hi, pt.lo, pt.hi & 0x7FFFFFFFFFFFFFFFull);
+  }
+  block_reduce(lo, hi, bad);
   __shared__ uint32_t s_last;
   if (threadIdx.x == 0) {
-    Partial pt;
-    pt.lo = qlo;
-    pt.hi = qhi;
-    pt.bad = bad;
-    pt.pad[0] = pt.pad[1] = pt.pad[2] = 0;
-    partials[blockIdx.x] = pt;
+    level2[blockIdx.x] = Partial{lo, hi | ((uint64_t)(bad ? 1u : 0u) << 63)};
     __threadfence();
     const uint32_t prev = atomicAdd(ticket, 1u);
     s_last = (prev == gridDim.x - 1) ? 1u : 0u;
@@ -237,16 +292,16 @@ __global__ __launch_bounds__(kThreads) void k1_reduce_check(
   __syncthreads();
   if (!s_last) return;
   __threadfence();
-  uint64_t tlo = 0, thi = 0;
-  uint32_t tbad = 0;
+  lo = hi = 0;
+  bad = 0;
   for (uint32_t i = threadIdx.x; i < gridDim.x; i += kThreads) {
-    const Partial pt = partials[i];
-    add128(tlo, thi, pt.lo, pt.hi);
-    tbad |= pt.bad;
+    const Partial pt = level2[i];
+    bad |= (uint32_t)(pt.hi >> 63);
+    add128(lo, hi, pt.lo, pt.hi & 0x7FFFFFFFFFFFFFFFull);
   }
-  block_reduce(tlo, thi, tbad);
+  block_reduce(lo, hi, bad);
   if (threadIdx.x == 0) {
-    finalize_into(tlo, thi, tbad, fa, res);
+    finalize_into(lo, hi, bad, fa, res);
     *ticket = 0u;  // ready for the next call
   }
 }
@@ -257,7 +312,10 @@ __global__ void k_finalize(FinalizeArgs fa, zero_step_result_t* res) {
 }
 
 // ---------------------------------------------------------------------------
-// K2: AdamW on the shard and the fp16 cast into the slot.
+// K2: AdamW on the shard and the fp16 cast into the slot.  Thread t of
+// workgroup b owns quads (4 elements) b*256*Q + u*256 + t, u < Q, so every
+// fp32 load and store instruction of a wave covers 1 KiB and every slot store
+// 512 bytes.
 __device__ __forceinline__ void adam1(float g, float c, const AdamScalars& sc, float& p, float& m,
                                       float& v) {
   const float gc = g * c;
@@ -274,51 +332,52 @@ __global__ __launch_bounds__(kThreads) void k2_adam(
     const zero_step_result_t* __restrict__ res) {
   if (res->skip) return;
   const float c = res->clip_coef;
-  const bool slot_aligned = (((uintptr_t)slot) & 15u) == 0;
-  const int64_t full = shard >> 3;
-  const int64_t total = (shard + 7) >> 3;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t grp = (int64_t)blockIdx.x * kThreads + threadIdx.x; grp < total; grp += stride) {
-    if (grp < full) {
-      const int64_t off = grp * 8;
-      f32x4 g[2], p[2], m[2], v[2];
+  const uint32_t slot_mis = (uint32_t)((uintptr_t)slot & 7u);  // 0: 8-byte stores
+  const int64_t full = shard >> 2;
+  f32x4 g[ZK_K2_QUADS], p[ZK_K2_QUADS], m[ZK_K2_QUADS], v[ZK_K2_QUADS];
+  int64_t qd[ZK_K2_QUADS];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        g[h] = __builtin_nontemporal_load((const f32x4*)(grad + off + 4 * h));
-        p[h] = __builtin_nontemporal_load((const f32x4*)(master + off + 4 * h));
-        m[h] = __builtin_nontemporal_load((const f32x4*)(mom + off + 4 * h));
-        v[h] = __builtin_nontemporal_load((const f32x4*)(var + off + 4 * h));
+  for (int u = 0; u < ZK_K2_QUADS; ++u) {
+    qd[u] = ((int64_t)blockIdx.x * ZK_K2_QUADS + u) * kThreads + threadIdx.x;
+    if (qd[u] < full) {
+      const int64_t off = qd[u] * 4;
+      g[u] = load16<ZK_K2_NT_LOAD>((const f32x4*)(grad + off));
+      p[u] = load16<ZK_K2_NT_LOAD>((const f32x4*)(master + off));
+      m[u] = load16<ZK_K2_NT_LOAD>((const f32x4*)(mom + off));
+      v[u] = load16<ZK_K2_NT_LOAD>((const f32x4*)(var + off));
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < ZK_K2_QUADS; ++u) {
+    if (qd[u] < full) {
+      const int64_t off = qd[u] * 4;
+      uint32_t hb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float pp = p[u][e], mm = m[u][e], vv = v[u][e];
+        adam1(g[u][e], c, sc, pp, mm, vv);
+        p[u][e] = pp;
+        m[u][e] = mm;
+        v[u][e] = vv;
+        hb[e] = f2h(pp);
       }
-      uint32_t hb[8];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pp = p[h][e], mm = m[h][e], vv = v[h][e];
-          adam1(g[h][e], c, sc, pp, mm, vv);
-          p[h][e] = pp;
-          m[h][e] = mm;
-          v[h][e] = vv;
-          hb[4 * h + e] = f2h(pp);
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        __builtin_nontemporal_store(p[h], (f32x4*)(master + off + 4 * h));
-        __builtin_nontemporal_store(m[h], (f32x4*)(mom + off + 4 * h));
-        __builtin_nontemporal_store(v[h], (f32x4*)(var + off + 4 * h));
-      }
-      if (slot_aligned) {
-        u32x4 o;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) o[w] = hb[2 * w] | (hb[2 * w + 1] << 16);
-        __builtin_nontemporal_store(o, (u32x4*)(slot + off));
+      store16<ZK_K2_NT_STORE>(p[u], (f32x4*)(master + off));
+      store16<ZK_K2_NT_STORE>(m[u], (f32x4*)(mom + off));
+      store16<ZK_K2_NT_STORE>(v[u], (f32x4*)(var + off));
+      if (slot_mis == 0) {
+        u32x2 o;
+        o[0] = hb[0] | (hb[1] << 16);
+        o[1] = hb[2] | (hb[3] << 16);
+        *(u32x2*)(slot + off) = o;
+      } else if ((slot_mis & 3u) == 0) {
+        *(uint32_t*)(slot + off) = hb[0] | (hb[1] << 16);
+        *(uint32_t*)(slot + off + 2) = hb[2] | (hb[3] << 16);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) slot[off + e] = (uint16_t)hb[e];
+        for (int e = 0; e < 4; ++e) slot[off + e] = (uint16_t)hb[e];
       }
-    } else {
-      for (int64_t j = grp * 8; j < shard; ++j) {
+    } else if (qd[u] == full) {
+      for (int64_t j = full * 4; j < shard; ++j) {
         float pp = master[j], mm = mom[j], vv = var[j];
         adam1(grad[j], c, sc, pp, mm, vv);
         master[j] = pp;
@@ -330,33 +389,19 @@ __global__ __launch_bounds__(kThreads) void k2_adam(
   }
 }
 
-// ---------------------------------------------------------------------------
-int g_cu_count[64];
-
-int cu_count() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && g_cu_count[dev] > 0) return g_cu_count[dev];
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
-  if (dev < 64) g_cu_count[dev] = cus;
-  return cus;
-}
-
-// Workgroups for a streaming pass over `groups` 8-element groups: enough for
-// eight resident workgroups per CU, never more than there are groups.
-int stream_blocks(int64_t groups, int per_cu) {
-  int64_t want = (groups + kThreads - 1) / kThreads;
-  int64_t cap = (int64_t)cu_count() * per_cu;
-  if (cap > kMaxBlocks) cap = kMaxBlocks;
-  if (want > cap) want = cap;
-  if (want < 1) want = 1;
-  return (int)want;
-}
-
 }  // namespace
+
+int64_t k1_blocks(int64_t shard) {
+  const int64_t groups = (shard + 7) >> 3;  // the ragged group included
+  const int64_t per = (int64_t)kThreads * ZK_K1_GROUPS;
+  const int64_t b = (groups + per - 1) / per;
+  return b < 1 ? 1 : b;
+}
+
+size_t workspace_bytes(int64_t shard) {
+  return kTicketBytes + (size_t)kFinBlocks * sizeof(Partial) +
+         (size_t)k1_blocks(shard) * sizeof(Partial);
+}
 
 int launch_reduce_check(const uint16_t* const* contrib, int n, int64_t shard, float inv32,
                         float* grad, void* workspace, const FinalizeArgs& fa,
@@ -364,10 +409,18 @@ int launch_reduce_check(const uint16_t* const* contrib, int n, int64_t shard, fl
   ContribTable ct;
   for (int r = 0; r < ZERO_MAX_RANKS; ++r) ct.p[r] = r < n ? contrib[r] : nullptr;
   uint32_t* ticket = (uint32_t*)workspace;
-  Partial* partials = (Partial*)((char*)workspace + kTicketBytes);
-  const int blocks = stream_blocks((shard + 7) >> 3, 8);
-  hipLaunchKernelGGL(k1_reduce_check, dim3(blocks), dim3(kThreads), 0, stream, ct, n, shard, inv32,
-                     grad, partials, ticket, fa, res);
+  Partial* level2 = (Partial*)((char*)workspace + kTicketBytes);
+  Partial* partials = level2 + kFinBlocks;
+  const int64_t blocks = k1_blocks(shard);
+  hipLaunchKernelGGL(k1_reduce_check, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, ct, n,
+                     shard, inv32, grad, partials);
+  int e = (int)hipGetLastError();
+  if (e != hipSuccess) return e;
+  int64_t fb = (blocks + kThreads * 4 - 1) / (kThreads * 4);
+  if (fb > kFinBlocks) fb = kFinBlocks;
+  if (fb < 1) fb = 1;
+  hipLaunchKernelGGL(kf_reduce_finalize, dim3((uint32_t)fb), dim3(kThreads), 0, stream, partials,
+                     blocks, level2, ticket, fa, res);
   return (int)hipGetLastError();
 }
 
@@ -379,9 +432,12 @@ int launch_finalize(const FinalizeArgs& fa, zero_step_result_t* res, hipStream_t
 int launch_adam(const float* grad, float* master, float* m, float* v, uint16_t* slot,
                 int64_t shard, const AdamScalars& sc, const zero_step_result_t* res,
                 hipStream_t stream) {
-  const int blocks = stream_blocks((shard + 7) >> 3, 8);
-  hipLaunchKernelGGL(k2_adam, dim3(blocks), dim3(kThreads), 0, stream, grad, master, m, v, slot,
-                     shard, sc, res);
+  const int64_t quads = (shard + 3) >> 2;
+  const int64_t per = (int64_t)kThreads * ZK_K2_QUADS;
+  int64_t blocks = (quads + per - 1) / per;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k2_adam, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, grad, master, m,
+                     v, slot, shard, sc, res);
   return (int)hipGetLastError();
 }
 

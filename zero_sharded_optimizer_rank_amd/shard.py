@@ -62,7 +62,8 @@ class DeviceShard:
         self.slot_buf = torch.full((GUARD + 8 + count + GUARD,), GUARD_WORD, dtype=torch.int16,
                                    device=self.device)
         self.slot_off = GUARD + self.mis
-        self.ws = torch.zeros(abi.zero_workspace_bytes(), dtype=torch.uint8, device=self.device)
+        self.ws = torch.zeros(abi.zero_workspace_bytes(self.plan), dtype=torch.uint8,
+                              device=self.device)
         self.res = torch.zeros(abi.RESULT_BYTES, dtype=torch.uint8, device=self.device)
         chunk = min(CHUNK, max(count, 1))
         self._pin16 = [torch.empty(chunk, dtype=torch.int16, pin_memory=True) for _ in range(2)]
