@@ -32,10 +32,19 @@
 
 // Launch shape and cache hints (compile-time; measured on MI355X).
 #ifndef ZK_K1_GROUPS
-#define ZK_K1_GROUPS 1  // 8-element groups per K1 thread
+#define ZK_K1_GROUPS 1  // 8-element groups per K1 thread (16-byte row loads)
+#endif
+#ifndef ZK_K1_QUADS
+#define ZK_K1_QUADS 1  // if > 0: 4-element quads per K1 thread (8-byte row loads) instead
 #endif
 #ifndef ZK_K2_QUADS
-#define ZK_K2_QUADS 2  // 4-element quads per K2 thread
+#define ZK_K2_QUADS 1  // 4-element quads per K2 thread
+#endif
+#ifndef ZK_K1_THREADS
+#define ZK_K1_THREADS 512  // threads per K1 workgroup (a multiple of 64)
+#endif
+#ifndef ZK_K2_THREADS
+#define ZK_K2_THREADS 64  // threads per K2 workgroup
 #endif
 #ifndef ZK_K1_NT_LOAD
 #define ZK_K1_NT_LOAD 1
@@ -71,13 +80,13 @@ static_assert(sizeof(Partial) == kPartialBytes, "partial layout");
 constexpr int kRankBatch = 8;  // contribution rows loaded before they are summed
 
 template <bool NT, typename T>
-__device__ __forceinline__ T load16(const T* p) {
+__device__ __forceinline__ T vload(const T* p) {
   if constexpr (NT) return __builtin_nontemporal_load(p);
   else return *p;
 }
 
 template <bool NT, typename T>
-__device__ __forceinline__ void store16(T v, T* p) {
+__device__ __forceinline__ void vstore(T v, T* p) {
   if constexpr (NT) __builtin_nontemporal_store(v, p);
   else *p = v;
 }
@@ -124,14 +133,17 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int mask) {
   return (uint64_t)__shfl_xor((long long)x, mask);
 }
 
-// Sum (lo, hi, bad) over the workgroup; the result is valid in thread 0.
+// Sum (lo, hi, bad) over a workgroup of T threads; valid in thread 0.
+template <int T>
 __device__ void block_reduce(uint64_t& lo, uint64_t& hi, uint32_t& bad) {
-  __shared__ uint64_t s_lo[kThreads / 64], s_hi[kThreads / 64];
-  __shared__ uint32_t s_bad[kThreads / 64];
+  static_assert(T % 64 == 0, "whole waves");
   for (int off = 32; off > 0; off >>= 1) {
     add128(lo, hi, shfl_xor_u64(lo, off), shfl_xor_u64(hi, off));
     bad |= (uint32_t)__shfl_xor((int)bad, off);
   }
+  if constexpr (T == 64) return;
+  __shared__ uint64_t s_lo[T / 64], s_hi[T / 64];
+  __shared__ uint32_t s_bad[T / 64];
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     s_lo[wave] = lo;
@@ -140,7 +152,7 @@ __device__ void block_reduce(uint64_t& lo, uint64_t& hi, uint32_t& bad) {
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < kThreads / 64; ++w) {
+    for (int w = 1; w < T / 64; ++w) {
       add128(lo, hi, s_lo[w], s_hi[w]);
       bad |= s_bad[w];
     }
@@ -211,7 +223,7 @@ __device__ __forceinline__ void reduce_group(const ContribTable& ct, int32_t n, 
     u32x4 d[kRankBatch];
 #pragma unroll
     for (int b = 0; b < kRankBatch; ++b)
-      if (r0 + b < n) d[b] = load16<ZK_K1_NT_LOAD>((const u32x4*)(ct.p[r0 + b] + off));
+      if (r0 + b < n) d[b] = vload<ZK_K1_NT_LOAD>((const u32x4*)(ct.p[r0 + b] + off));
 #pragma unroll
     for (int b = 0; b < kRankBatch; ++b) {
       if (r0 + b < n) {
@@ -229,8 +241,8 @@ __device__ __forceinline__ void reduce_group(const ContribTable& ct, int32_t n, 
     g0[e] = acc[e] * inv32;
     g1[e] = acc[4 + e] * inv32;
   }
-  store16<ZK_K1_NT_STORE>(g0, (f32x4*)(grad + off));
-  store16<ZK_K1_NT_STORE>(g1, (f32x4*)(grad + off + 4));
+  vstore<ZK_K1_NT_STORE>(g0, (f32x4*)(grad + off));
+  vstore<ZK_K1_NT_STORE>(g1, (f32x4*)(grad + off + 4));
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     uint64_t lo, hi;
@@ -239,31 +251,85 @@ __device__ __forceinline__ void reduce_group(const ContribTable& ct, int32_t n, 
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k1_reduce_check(ContribTable ct, int32_t n,
-                                                            int64_t shard, float inv32,
-                                                            float* __restrict__ grad,
-                                                            Partial* __restrict__ partials) {
-  const int64_t full = shard >> 3;
-  uint64_t qlo = 0, qhi = 0;
-  uint32_t bad = 0;
+// Quad form: 8-byte row loads, and each gradient store instruction of a wave
+// writes 1 KiB contiguous.
+__device__ __forceinline__ void reduce_quad(const ContribTable& ct, int32_t n, int64_t qd,
+                                            float inv32, float* __restrict__ grad,
+                                            uint64_t& qlo, uint64_t& qhi, uint32_t& bad) {
+  const int64_t off = qd * 4;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int r0 = 0; r0 < n; r0 += kRankBatch) {
+    u32x2 d[kRankBatch];
 #pragma unroll
-  for (int u = 0; u < ZK_K1_GROUPS; ++u) {
-    const int64_t grp = ((int64_t)blockIdx.x * ZK_K1_GROUPS + u) * kThreads + threadIdx.x;
-    if (grp < full) {
-      reduce_group(ct, n, grp, inv32, grad, qlo, qhi, bad);
-    } else if (grp == full) {
-      // ragged tail: the last shard % 8 elements
-      for (int64_t j = grp * 8; j < shard; ++j) {
-        float a = 0.0f;
-        for (int r = 0; r < n; ++r) a = a + h2f(ct.p[r][j]);
-        grad[j] = a * inv32;
-        uint64_t lo, hi;
-        sq_units(a, lo, hi, bad);
-        add128(qlo, qhi, lo, hi);
+    for (int b = 0; b < kRankBatch; ++b)
+      if (r0 + b < n) d[b] = vload<ZK_K1_NT_LOAD>((const u32x2*)(ct.p[r0 + b] + off));
+#pragma unroll
+    for (int b = 0; b < kRankBatch; ++b) {
+      if (r0 + b < n) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          acc[2 * w] = acc[2 * w] + h2f(d[b][w] & 0xFFFFu);
+          acc[2 * w + 1] = acc[2 * w + 1] + h2f(d[b][w] >> 16);
+        }
       }
     }
   }
-  block_reduce(qlo, qhi, bad);
+  f32x4 g;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) g[e] = acc[e] * inv32;
+  vstore<ZK_K1_NT_STORE>(g, (f32x4*)(grad + off));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint64_t lo, hi;
+    sq_units(acc[e], lo, hi, bad);
+    add128(qlo, qhi, lo, hi);
+  }
+}
+
+__global__ __launch_bounds__(ZK_K1_THREADS) void k1_reduce_check(ContribTable ct, int32_t n,
+                                                            int64_t shard, float inv32,
+                                                            float* __restrict__ grad,
+                                                            Partial* __restrict__ partials) {
+  uint64_t qlo = 0, qhi = 0;
+  uint32_t bad = 0;
+  int64_t tail_from;  // first element of the ragged tail, handled by one thread
+  bool tail_owner;
+  if constexpr (ZK_K1_QUADS > 0) {
+    const int64_t full = shard >> 2;
+#pragma unroll
+    for (int u = 0; u < ZK_K1_QUADS; ++u) {
+      const int64_t qd = ((int64_t)blockIdx.x * ZK_K1_QUADS + u) * ZK_K1_THREADS + threadIdx.x;
+      if (qd < full) reduce_quad(ct, n, qd, inv32, grad, qlo, qhi, bad);
+    }
+    // the thread that would own quad `full` takes the tail
+    tail_from = full * 4;
+    const int64_t per = (int64_t)ZK_K1_THREADS * ZK_K1_QUADS;
+    const int64_t b = full / per, rem = full % per;
+    tail_owner = (int64_t)blockIdx.x == b && (int64_t)threadIdx.x == rem % ZK_K1_THREADS;
+  } else {
+    const int64_t full = shard >> 3;
+#pragma unroll
+    for (int u = 0; u < ZK_K1_GROUPS; ++u) {
+      const int64_t grp = ((int64_t)blockIdx.x * ZK_K1_GROUPS + u) * ZK_K1_THREADS + threadIdx.x;
+      if (grp < full) reduce_group(ct, n, grp, inv32, grad, qlo, qhi, bad);
+    }
+    tail_from = full * 8;
+    const int64_t per = (int64_t)ZK_K1_THREADS * ZK_K1_GROUPS;
+    const int64_t b = full / per, rem = full % per;
+    tail_owner = (int64_t)blockIdx.x == b && (int64_t)threadIdx.x == rem % ZK_K1_THREADS;
+  }
+  if (tail_owner) {
+    // ragged tail: the last shard % 4 (or % 8) elements
+    for (int64_t j = tail_from; j < shard; ++j) {
+      float a = 0.0f;
+      for (int r = 0; r < n; ++r) a = a + h2f(ct.p[r][j]);
+      grad[j] = a * inv32;
+      uint64_t lo, hi;
+      sq_units(a, lo, hi, bad);
+      add128(qlo, qhi, lo, hi);
+    }
+  }
+  block_reduce<ZK_K1_THREADS>(qlo, qhi, bad);
   if (threadIdx.x == 0) partials[blockIdx.x] = Partial{qlo, qhi | ((uint64_t)(bad ? 1u : 0u) << 63)};
 }
 
@@ -281,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void kf_reduce_finalize(
     bad |= (uint32_t)(pt.hi >> 63);
     add128(lo, hi, pt.lo, pt.hi & 0x7FFFFFFFFFFFFFFFull);
   }
-  block_reduce(lo, hi, bad);
+  block_reduce<kThreads>(lo, hi, bad);
   __shared__ uint32_t s_last;
   if (threadIdx.x == 0) {
     level2[blockIdx.x] = Partial{lo, hi | ((uint64_t)(bad ? 1u : 0u) << 63)};
@@ -299,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void kf_reduce_finalize(
     bad |= (uint32_t)(pt.hi >> 63);
     add128(lo, hi, pt.lo, pt.hi & 0x7FFFFFFFFFFFFFFFull);
   }
-  block_reduce(lo, hi, bad);
+  block_reduce<kThreads>(lo, hi, bad);
   if (threadIdx.x == 0) {
     finalize_into(lo, hi, bad, fa, res);
     *ticket = 0u;  // ready for the next call
@@ -313,7 +379,7 @@ __global__ void k_finalize(FinalizeArgs fa, zero_step_result_t* res) {
 
 // ---------------------------------------------------------------------------
 // K2: AdamW on the shard and the fp16 cast into the slot.  Thread t of
-// workgroup b owns quads (4 elements) b*256*Q + u*256 + t, u < Q, so every
+// workgroup b owns quads (4 elements) (b*Q + u)*T + t, u < Q, so every
 // fp32 load and store instruction of a wave covers 1 KiB and every slot store
 // 512 bytes.
 __device__ __forceinline__ void adam1(float g, float c, const AdamScalars& sc, float& p, float& m,
@@ -326,7 +392,7 @@ __device__ __forceinline__ void adam1(float g, float c, const AdamScalars& sc, f
   p = p * sc.decay - u;
 }
 
-__global__ __launch_bounds__(kThreads) void k2_adam(
+__global__ __launch_bounds__(ZK_K2_THREADS) void k2_adam(
     const float* __restrict__ grad, float* __restrict__ master, float* __restrict__ mom,
     float* __restrict__ var, uint16_t* __restrict__ slot, int64_t shard, AdamScalars sc,
     const zero_step_result_t* __restrict__ res) {
@@ -338,13 +404,13 @@ __global__ __launch_bounds__(kThreads) void k2_adam(
   int64_t qd[ZK_K2_QUADS];
 #pragma unroll
   for (int u = 0; u < ZK_K2_QUADS; ++u) {
-    qd[u] = ((int64_t)blockIdx.x * ZK_K2_QUADS + u) * kThreads + threadIdx.x;
+    qd[u] = ((int64_t)blockIdx.x * ZK_K2_QUADS + u) * ZK_K2_THREADS + threadIdx.x;
     if (qd[u] < full) {
       const int64_t off = qd[u] * 4;
-      g[u] = load16<ZK_K2_NT_LOAD>((const f32x4*)(grad + off));
-      p[u] = load16<ZK_K2_NT_LOAD>((const f32x4*)(master + off));
-      m[u] = load16<ZK_K2_NT_LOAD>((const f32x4*)(mom + off));
-      v[u] = load16<ZK_K2_NT_LOAD>((const f32x4*)(var + off));
+      g[u] = vload<ZK_K2_NT_LOAD>((const f32x4*)(grad + off));
+      p[u] = vload<ZK_K2_NT_LOAD>((const f32x4*)(master + off));
+      m[u] = vload<ZK_K2_NT_LOAD>((const f32x4*)(mom + off));
+      v[u] = vload<ZK_K2_NT_LOAD>((const f32x4*)(var + off));
     }
   }
 #pragma unroll
@@ -361,9 +427,9 @@ __global__ __launch_bounds__(kThreads) void k2_adam(
         v[u][e] = vv;
         hb[e] = f2h(pp);
       }
-      store16<ZK_K2_NT_STORE>(p[u], (f32x4*)(master + off));
-      store16<ZK_K2_NT_STORE>(m[u], (f32x4*)(mom + off));
-      store16<ZK_K2_NT_STORE>(v[u], (f32x4*)(var + off));
+      vstore<ZK_K2_NT_STORE>(p[u], (f32x4*)(master + off));
+      vstore<ZK_K2_NT_STORE>(m[u], (f32x4*)(mom + off));
+      vstore<ZK_K2_NT_STORE>(v[u], (f32x4*)(var + off));
       if (slot_mis == 0) {
         u32x2 o;
         o[0] = hb[0] | (hb[1] << 16);
@@ -392,9 +458,10 @@ __global__ __launch_bounds__(kThreads) void k2_adam(
 }  // namespace
 
 int64_t k1_blocks(int64_t shard) {
-  const int64_t groups = (shard + 7) >> 3;  // the ragged group included
-  const int64_t per = (int64_t)kThreads * ZK_K1_GROUPS;
-  const int64_t b = (groups + per - 1) / per;
+  // units of 4 or 8 elements, the ragged unit included
+  const int64_t units = ZK_K1_QUADS > 0 ? (shard + 3) >> 2 : (shard + 7) >> 3;
+  const int64_t per = (int64_t)ZK_K1_THREADS * (ZK_K1_QUADS > 0 ? ZK_K1_QUADS : ZK_K1_GROUPS);
+  const int64_t b = (units + per - 1) / per;
   return b < 1 ? 1 : b;
 }
 
@@ -412,7 +479,7 @@ int launch_reduce_check(const uint16_t* const* contrib, int n, int64_t shard, fl
   Partial* level2 = (Partial*)((char*)workspace + kTicketBytes);
   Partial* partials = level2 + kFinBlocks;
   const int64_t blocks = k1_blocks(shard);
-  hipLaunchKernelGGL(k1_reduce_check, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, ct, n,
+  hipLaunchKernelGGL(k1_reduce_check, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), 0, stream, ct, n,
                      shard, inv32, grad, partials);
   int e = (int)hipGetLastError();
   if (e != hipSuccess) return e;
@@ -433,10 +500,10 @@ int launch_adam(const float* grad, float* master, float* m, float* v, uint16_t* 
                 int64_t shard, const AdamScalars& sc, const zero_step_result_t* res,
                 hipStream_t stream) {
   const int64_t quads = (shard + 3) >> 2;
-  const int64_t per = (int64_t)kThreads * ZK_K2_QUADS;
+  const int64_t per = (int64_t)ZK_K2_THREADS * ZK_K2_QUADS;
   int64_t blocks = (quads + per - 1) / per;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(k2_adam, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, grad, master, m,
+  hipLaunchKernelGGL(k2_adam, dim3((uint32_t)blocks), dim3(ZK_K2_THREADS), 0, stream, grad, master, m,
                      v, slot, shard, sc, res);
   return (int)hipGetLastError();
 }
