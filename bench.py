@@ -179,12 +179,12 @@ def main():
         src = torch.empty(nb, dtype=torch.uint8, device="cuda")
         dst = torch.empty(nb, dtype=torch.uint8, device="cuda")
         best = None
-        for blocks in (2048, 4096, 8192):
+        for threads in (64, 256):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             for rep in range(4):
                 if rep == 1:
                     e0.record(stream)
-                rc = cl.zero_calib_copy(src.data_ptr(), dst.data_ptr(), nb, blocks,
+                rc = cl.zero_calib_copy(src.data_ptr(), dst.data_ptr(), nb, threads,
                                         stream.cuda_stream)
                 assert rc == 0
             e1.record(stream)

@@ -1,0 +1,136 @@
+"""GPU parity at the workloads' full shard sizes, in the launch configuration
+bench.py times (the whole shard of the rank).
+
+Every step of each workload runs on the GPU.  The oracle checks:
+  * the exact squared-norm integer, overflow flag, norm, clip coefficient and
+    skip decision of the whole shard (computed by the C form of the oracle's
+    reduce statistics from the same host-generated input chunks that are
+    copied to the device);
+  * g, master, m, v and the fp16 slot at ~4k sampled elements (first, last,
+    random, and around an injected inf), computed one by one by the numpy
+    oracle, bit for bit, with the state carried across steps.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import fast
+from oracle import run as orun
+
+from parity_util import check_result, compare_state, other_overflow_at, StepReport
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _sample_indices(w, rank, shard, k=4096):
+    rng = np.random.default_rng(7 + rank)
+    idx = set(rng.integers(0, shard, size=k).tolist())
+    idx.update(range(0, 32))
+    idx.update(range(max(0, shard - 32), shard))
+    site = synth.inject_site(w, w.inject_step) if w.inject_step else None
+    if site is not None:
+        p = orun.workload_plan(w)
+        j = site[1] - rank * p.shard
+        if 0 <= j < shard:
+            idx.update(range(max(0, j - 8), min(shard, j + 9)))
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+def _feed_and_reduce(dev, step, scale, idx):
+    """Generate the step's contributions chunk by chunk on the host, copy each
+    chunk to the device, and reduce the same chunk with the C oracle.  Returns
+    (Q, overflow, contributions at idx)."""
+    w, n, count = dev.w, dev.w.world_size, dev.count
+    chunk = (1 << 28) // (2 * n)  # 256 MiB of host staging
+    host = torch.empty((n, chunk), dtype=torch.int16, pin_memory=True)
+    hnp = host.numpy().view(np.uint16)
+    q_total, bad = 0, False
+    cols = np.zeros((n, idx.size), dtype=np.uint16)
+    for c0 in range(0, count, chunk):
+        k = min(chunk, count - c0)
+        for q in range(n):
+            synth.contributions(w, step, q, dev.flat_begin + c0, k, scale, out=hnp[q, :k])
+        with torch.cuda.stream(dev.stream):
+            for q in range(n):
+                dev.contrib[q, c0:c0 + k].copy_(host[q, :k], non_blocking=True)
+        qc, bc = fast.reduce_stats(hnp, k)
+        q_total += qc
+        bad |= bc
+        sel = (idx >= c0) & (idx < c0 + k)
+        cols[:, sel] = hnp[:, idx[sel] - c0]
+        dev.stream.synchronize()
+    return q_total, bad, cols
+
+
+def _cases():
+    return [pytest.param(w, r, id=f"{w.name}-r{r}") for w, r in (
+        (synth.GPT2, 0), (synth.GPT2, 1), (synth.GPT2, 63),
+        (synth.FLAT75, 0), (synth.FLAT75, 1),
+        (synth.LLAMA3_8B, 0),
+        (synth.LLAMA2_70B, 0),
+    )]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("w,rank", _cases())
+def test_full_size_shard(w, rank):
+    import zero_sharded_optimizer_rank_amd.abi as abi
+    from zero_sharded_optimizer_rank_amd.shard import DeviceShard
+
+    print(f"[full size {w.name} rank {rank}]", flush=True)
+    dev = DeviceShard(w, rank)
+    dev.load_initial_state()
+    p = orun.workload_plan(w)
+    assert dev.count == p.shard and dev.flat_begin == rank * p.shard
+    idx = _sample_indices(w, rank, p.shard)
+    flat = rank * p.shard + idx
+    op = np.array([synth.masters(w, int(e), 1)[0] for e in flat], dtype=np.float32)
+    om, ov = np.zeros_like(op), np.zeros_like(op)
+    oh = op.astype(np.float16).view(np.uint16)
+    other_sq = w.other_sq(p.real(rank)) if w.other_ranks_from_config else 0.0
+    scaler = abi.new_scaler(w.loss_scale0)
+    o_scale, o_good, o_t = w.loss_scale0, 0, 0
+    skips = []
+    for step in range(1, w.steps + 1):
+        ovf_other = other_overflow_at(w, step, dev.flat_begin, dev.count)
+        q_all, bad_all, cols = _feed_and_reduce(dev, step, scaler.scale, idx)
+        args = dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq, other_overflow=ovf_other)
+        dev.step(args)
+        res = dev.result()
+        sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, o_t + 1, w.world_size,
+                                 o_scale)
+        fin = oracle.finalize(q_all, bad_all, sc.inv64, w.max_grad_norm, other_sq=other_sq,
+                              other_overflow=ovf_other)
+        check_result(res, fin, step)
+        acc = oracle.reduce_contributions(cols)
+        g = oracle.unscale(acc, sc.inv32)
+        assert np.array_equal(dev.fetch("grad", idx).view(np.uint32), g.view(np.uint32)), step
+        if not fin.skip:
+            op, om, ov, h = oracle.adam_apply(g, op, om, ov, sc, fin.coef)
+            oh = h.view(np.uint16)
+        rep = StepReport(step, fin.skip, float(fin.coef))
+        for name, want in (("master", op), ("m", om), ("v", ov), ("slot", oh)):
+            compare_state(rep, name, dev.fetch(name, idx), want)
+        assert all(x == 0 for x in rep.mismatches.values()), (step, rep.mismatches)
+        assert dev.guards_intact()
+        print(f"  step {step}: skip={fin.skip} coef={float(fin.coef):.6g} norm={fin.norm:.6g} "
+              f"Q bits={q_all.bit_length()}", flush=True)
+        skips.append(fin.skip)
+        abi.zero_scaler_update(scaler, bool(res.skip))
+        o_scale, o_good = oracle.scaler_update(o_scale, o_good, fin.skip)
+        o_t += 0 if fin.skip else 1
+        assert scaler.t == o_t and scaler.scale == o_scale
+    if w.inject_step is not None and rank == 0:
+        assert skips[w.inject_step - 1] and not any(s for i, s in enumerate(skips)
+                                                    if i != w.inject_step - 1)
+    del dev
+    torch.cuda.empty_cache()

@@ -1,0 +1,42 @@
+"""Pin: the C form of the oracle's reduce statistics equals the numpy
+definition (and Python big integers) bit for bit."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import fast
+
+
+@pytest.mark.parametrize("n", [1, 3, 8, 64])
+def test_c_stats_equal_numpy(n):
+    rng = np.random.default_rng(100 + n)
+    for scale in (1e-4, 1.0, 300.0):
+        c = (rng.standard_normal((n, 40_001)) * scale).astype(np.float16).view(np.uint16)
+        q, bad = fast.reduce_stats(c)
+        acc = oracle.reduce_contributions(c)
+        assert q == oracle.exact_sq_units(acc) and bad == oracle.nonfinite(acc)
+
+
+def test_c_stats_nonfinite_and_extremes():
+    c = np.zeros((64, 9), dtype=np.float16)
+    c[:, 0] = 65504.0
+    c[:, 1] = -65504.0
+    c[:, 2] = 2.0**-24
+    c[3, 3] = -0.0
+    q, bad = fast.reduce_stats(c.view(np.uint16))
+    assert not bad and q == 2 * (64 * 65504 * 2**24) ** 2 + 64**2
+    for v in (np.inf, -np.inf, np.nan):
+        d = c.copy()
+        d[5, 7] = v
+        q2, bad2 = fast.reduce_stats(d.view(np.uint16))
+        assert bad2 and q2 == q  # the non-finite element adds nothing to Q
+
+
+def test_c_stats_subnormal_conversion():
+    # every fp16 bit pattern converts exactly (compare single-rank sums to numpy)
+    allbits = np.arange(65536, dtype=np.uint16)
+    finite = np.isfinite(allbits.view(np.float16))
+    rows = allbits[finite][None, :].copy()
+    q, bad = fast.reduce_stats(rows)
+    acc = oracle.reduce_contributions(rows)
+    assert not bad and q == oracle.exact_sq_units(acc)
