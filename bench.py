@@ -101,6 +101,8 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--row-align", type=int, default=None,
+                    help="contribution row stride alignment in elements (default: the runtime's)")
     ap.add_argument("--calib-bytes", type=float, default=4e9,
                     help="bytes of the calibration copy timed next to the step (0: skip)")
     a = ap.parse_args()
@@ -117,7 +119,7 @@ def main():
 
     abi.lib()
     w = synth.BY_NAME[a.workload]
-    dev = DeviceShard(w, a.rank)
+    dev = DeviceShard(w, a.rank, **({} if a.row_align is None else {"row_align": a.row_align}))
     stream = dev.stream
     n = w.world_size
     real = abi.zero_plan_real(dev.full_plan, a.rank)

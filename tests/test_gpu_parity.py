@@ -269,3 +269,11 @@ def test_argument_errors():
             abi.zero_reduce_adam_step(plan, kw["rank"], kw["contrib"], buf, buf, buf, kw["slot"],
                                       kw["grad"], ws, kw["ws_bytes"], kw["args"], res)
         assert e.value.code == code, (over, e.value)
+
+
+@pytest.mark.parametrize("begin", range(8))
+@pytest.mark.parametrize("count", [1, 3, 4, 5, 63, 255, 256, 257, 259, 1027, 70_001])
+def test_slot_offsets(begin, count):
+    """Every slot alignment (flat offset mod 8) with lengths that end inside a
+    quad, a wave or several waves: state and slot bit-exact, guards intact."""
+    run_window(synth.TINY, 0, begin, count, steps=2)

@@ -31,11 +31,8 @@
 #pragma clang fp contract(off)
 
 // Launch shape and cache hints (compile-time; measured on MI355X).
-#ifndef ZK_K1_GROUPS
-#define ZK_K1_GROUPS 1  // 8-element groups per K1 thread (16-byte row loads)
-#endif
 #ifndef ZK_K1_QUADS
-#define ZK_K1_QUADS 1  // if > 0: 4-element quads per K1 thread (8-byte row loads) instead
+#define ZK_K1_QUADS 1  // 4-element quads per K1 thread
 #endif
 #ifndef ZK_K2_QUADS
 #define ZK_K2_QUADS 1  // 4-element quads per K2 thread
@@ -133,6 +130,12 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int mask) {
   return (uint64_t)__shfl_xor((long long)x, mask);
 }
 
+__device__ __forceinline__ uint64_t shfl_down_u64(uint64_t x, unsigned int delta) {
+  const uint32_t lo = (uint32_t)__shfl_down((int)(uint32_t)x, delta);
+  const uint32_t hi = (uint32_t)__shfl_down((int)(uint32_t)(x >> 32), delta);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Sum (lo, hi, bad) over a workgroup of T threads; valid in thread 0.
 template <int T>
 __device__ void block_reduce(uint64_t& lo, uint64_t& hi, uint32_t& bad) {
@@ -210,49 +213,9 @@ __device__ void finalize_into(uint64_t qlo, uint64_t qhi, uint32_t bad, const Fi
 
 // ---------------------------------------------------------------------------
 // K1: reduce, unscale, overflow flag, exact squared norm, one partial per
-// workgroup.  Thread t of workgroup b owns groups b*256*G + u*256 + t,
-// u < G, so each load instruction of a wave covers 1 KiB of a row.
-__device__ __forceinline__ void reduce_group(const ContribTable& ct, int32_t n, int64_t grp,
-                                             float inv32, float* __restrict__ grad,
-                                             uint64_t& qlo, uint64_t& qhi, uint32_t& bad) {
-  const int64_t off = grp * 8;
-  float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-  for (int r0 = 0; r0 < n; r0 += kRankBatch) {
-    u32x4 d[kRankBatch];
-#pragma unroll
-    for (int b = 0; b < kRankBatch; ++b)
-      if (r0 + b < n) d[b] = vload<ZK_K1_NT_LOAD>((const u32x4*)(ct.p[r0 + b] + off));
-#pragma unroll
-    for (int b = 0; b < kRankBatch; ++b) {
-      if (r0 + b < n) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          acc[2 * w] = acc[2 * w] + h2f(d[b][w] & 0xFFFFu);
-          acc[2 * w + 1] = acc[2 * w + 1] + h2f(d[b][w] >> 16);
-        }
-      }
-    }
-  }
-  f32x4 g0, g1;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    g0[e] = acc[e] * inv32;
-    g1[e] = acc[4 + e] * inv32;
-  }
-  vstore<ZK_K1_NT_STORE>(g0, (f32x4*)(grad + off));
-  vstore<ZK_K1_NT_STORE>(g1, (f32x4*)(grad + off + 4));
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uint64_t lo, hi;
-    sq_units(acc[e], lo, hi, bad);
-    add128(qlo, qhi, lo, hi);
-  }
-}
-
-// Quad form: 8-byte row loads, and each gradient store instruction of a wave
-// writes 1 KiB contiguous.
+// workgroup.  Thread t of workgroup b owns quads (b*Q + u)*T + t, u < Q: each
+// loads 8 bytes from every row, so a wave's row load covers 512 contiguous
+// bytes and its gradient store 1 KiB.
 __device__ __forceinline__ void reduce_quad(const ContribTable& ct, int32_t n, int64_t qd,
                                             float inv32, float* __restrict__ grad,
                                             uint64_t& qlo, uint64_t& qhi, uint32_t& bad) {
@@ -292,34 +255,19 @@ __global__ __launch_bounds__(ZK_K1_THREADS) void k1_reduce_check(ContribTable ct
                                                             Partial* __restrict__ partials) {
   uint64_t qlo = 0, qhi = 0;
   uint32_t bad = 0;
-  int64_t tail_from;  // first element of the ragged tail, handled by one thread
-  bool tail_owner;
-  if constexpr (ZK_K1_QUADS > 0) {
-    const int64_t full = shard >> 2;
+  const int64_t full = shard >> 2;
 #pragma unroll
-    for (int u = 0; u < ZK_K1_QUADS; ++u) {
-      const int64_t qd = ((int64_t)blockIdx.x * ZK_K1_QUADS + u) * ZK_K1_THREADS + threadIdx.x;
-      if (qd < full) reduce_quad(ct, n, qd, inv32, grad, qlo, qhi, bad);
-    }
-    // the thread that would own quad `full` takes the tail
-    tail_from = full * 4;
-    const int64_t per = (int64_t)ZK_K1_THREADS * ZK_K1_QUADS;
-    const int64_t b = full / per, rem = full % per;
-    tail_owner = (int64_t)blockIdx.x == b && (int64_t)threadIdx.x == rem % ZK_K1_THREADS;
-  } else {
-    const int64_t full = shard >> 3;
-#pragma unroll
-    for (int u = 0; u < ZK_K1_GROUPS; ++u) {
-      const int64_t grp = ((int64_t)blockIdx.x * ZK_K1_GROUPS + u) * ZK_K1_THREADS + threadIdx.x;
-      if (grp < full) reduce_group(ct, n, grp, inv32, grad, qlo, qhi, bad);
-    }
-    tail_from = full * 8;
-    const int64_t per = (int64_t)ZK_K1_THREADS * ZK_K1_GROUPS;
-    const int64_t b = full / per, rem = full % per;
-    tail_owner = (int64_t)blockIdx.x == b && (int64_t)threadIdx.x == rem % ZK_K1_THREADS;
+  for (int u = 0; u < ZK_K1_QUADS; ++u) {
+    const int64_t qd = ((int64_t)blockIdx.x * ZK_K1_QUADS + u) * ZK_K1_THREADS + threadIdx.x;
+    if (qd < full) reduce_quad(ct, n, qd, inv32, grad, qlo, qhi, bad);
   }
+  // the thread that would own quad `full` takes the ragged tail
+  const int64_t tail_from = full * 4;
+  const int64_t per = (int64_t)ZK_K1_THREADS * ZK_K1_QUADS;
+  const bool tail_owner = (int64_t)blockIdx.x == full / per &&
+                          (int64_t)threadIdx.x == (full % per) % ZK_K1_THREADS;
   if (tail_owner) {
-    // ragged tail: the last shard % 4 (or % 8) elements
+    // ragged tail: the last shard % 4 elements
     for (int64_t j = tail_from; j < shard; ++j) {
       float a = 0.0f;
       for (int r = 0; r < n; ++r) a = a + h2f(ct.p[r][j]);
@@ -398,7 +346,10 @@ __global__ __launch_bounds__(ZK_K2_THREADS) void k2_adam(
     const zero_step_result_t* __restrict__ res) {
   if (res->skip) return;
   const float c = res->clip_coef;
-  const uint32_t slot_mis = (uint32_t)((uintptr_t)slot & 7u);  // 0: 8-byte stores
+  // slot misalignment in elements relative to 8-byte words (the slot may sit
+  // at any element offset of the flat buffer)
+  const uint32_t me = (uint32_t)(((uintptr_t)slot >> 1) & 3u);
+  const uint32_t lane = threadIdx.x & 63u;
   const int64_t full = shard >> 2;
   f32x4 g[ZK_K2_QUADS], p[ZK_K2_QUADS], m[ZK_K2_QUADS], v[ZK_K2_QUADS];
   int64_t qd[ZK_K2_QUADS];
@@ -415,9 +366,10 @@ __global__ __launch_bounds__(ZK_K2_THREADS) void k2_adam(
   }
 #pragma unroll
   for (int u = 0; u < ZK_K2_QUADS; ++u) {
-    if (qd[u] < full) {
-      const int64_t off = qd[u] * 4;
-      uint32_t hb[4];
+    const bool valid = qd[u] < full;
+    const int64_t off = qd[u] * 4;
+    uint64_t h = 0;  // the quad's four fp16 results, element e in bits 16e..16e+15
+    if (valid) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float pp = p[u][e], mm = m[u][e], vv = v[u][e];
@@ -425,24 +377,33 @@ __global__ __launch_bounds__(ZK_K2_THREADS) void k2_adam(
         p[u][e] = pp;
         m[u][e] = mm;
         v[u][e] = vv;
-        hb[e] = f2h(pp);
+        h |= (uint64_t)f2h(pp) << (16 * e);
       }
       vstore<ZK_K2_NT_STORE>(p[u], (f32x4*)(master + off));
       vstore<ZK_K2_NT_STORE>(m[u], (f32x4*)(mom + off));
       vstore<ZK_K2_NT_STORE>(v[u], (f32x4*)(var + off));
-      if (slot_mis == 0) {
-        u32x2 o;
-        o[0] = hb[0] | (hb[1] << 16);
-        o[1] = hb[2] | (hb[3] << 16);
-        *(u32x2*)(slot + off) = o;
-      } else if ((slot_mis & 3u) == 0) {
-        *(uint32_t*)(slot + off) = hb[0] | (hb[1] << 16);
-        *(uint32_t*)(slot + off + 2) = hb[2] | (hb[3] << 16);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) slot[off + e] = (uint16_t)hb[e];
+    }
+    if (me == 0) {
+      if (valid) *(uint64_t*)(slot + off) = h;
+    } else {
+      // Realign through the neighbour lane: lane i writes the aligned 8-byte
+      // word holding its last `me` results and lane i+1's first 4 - me.
+      // The pieces at a wave's edges or at the shard's end go out as 2-byte
+      // stores.  Every lane of the wave takes part in the shuffle.
+      const uint64_t hn = shfl_down_u64(h, 1);
+      const bool right = lane < 63u && qd[u] + 1 < full;
+      if (valid) {
+        if (lane == 0u) {
+          for (uint32_t e = 0; e < 4u - me; ++e) slot[off + e] = (uint16_t)(h >> (16 * e));
+        }
+        if (right) {
+          *(uint64_t*)(slot + off + 4 - me) = (h >> (16 * (4u - me))) | (hn << (16 * me));
+        } else {
+          for (uint32_t e = 4u - me; e < 4u; ++e) slot[off + e] = (uint16_t)(h >> (16 * e));
+        }
       }
-    } else if (qd[u] == full) {
+    }
+    if (qd[u] == full) {
       for (int64_t j = full * 4; j < shard; ++j) {
         float pp = master[j], mm = mom[j], vv = var[j];
         adam1(grad[j], c, sc, pp, mm, vv);
@@ -458,9 +419,8 @@ __global__ __launch_bounds__(ZK_K2_THREADS) void k2_adam(
 }  // namespace
 
 int64_t k1_blocks(int64_t shard) {
-  // units of 4 or 8 elements, the ragged unit included
-  const int64_t units = ZK_K1_QUADS > 0 ? (shard + 3) >> 2 : (shard + 7) >> 3;
-  const int64_t per = (int64_t)ZK_K1_THREADS * (ZK_K1_QUADS > 0 ? ZK_K1_QUADS : ZK_K1_GROUPS);
+  const int64_t units = (shard + 3) >> 2;  // quads, the ragged one included
+  const int64_t per = (int64_t)ZK_K1_THREADS * ZK_K1_QUADS;
   const int64_t b = (units + per - 1) / per;
   return b < 1 ? 1 : b;
 }

@@ -25,6 +25,7 @@ from . import abi
 GUARD = 64  # fp16 guard elements on each side of the slot
 GUARD_WORD = 0x5A5A
 CHUNK = 1 << 25  # elements per host staging chunk
+ROW_ALIGN = 128  # contribution rows start on 256-byte boundaries (whole cache lines)
 
 
 def round_up(x: int, a: int) -> int:
@@ -33,7 +34,8 @@ def round_up(x: int, a: int) -> int:
 
 class DeviceShard:
     def __init__(self, w: synth.Workload, rank: int, begin: int = 0, count: Optional[int] = None,
-                 device: str = "cuda:0", stream: Optional[torch.cuda.Stream] = None):
+                 device: str = "cuda:0", stream: Optional[torch.cuda.Stream] = None,
+                 row_align: int = ROW_ALIGN):
         self.w = w
         self.rank = rank
         self.device = torch.device(device)
@@ -50,7 +52,7 @@ class DeviceShard:
         n = w.world_size
         self.plan = abi.zero_plan_t(real, n, 1, count, count * n)
         self.stream = stream or torch.cuda.current_stream(self.device)
-        ld = round_up(max(count, 1), 8)
+        ld = round_up(max(count, 1), row_align)
         self.ld = ld
         self.contrib = torch.empty((n, ld), dtype=torch.int16, device=self.device)
         self.master = torch.empty(max(count, 1), dtype=torch.float32, device=self.device)
