@@ -384,7 +384,7 @@ __global__ __launch_bounds__(ZK_K2_THREADS) void k2_adam(
       vstore<ZK_K2_NT_STORE>(v[u], (f32x4*)(var + off));
     }
     if (me == 0) {
-      if (valid) *(uint64_t*)(slot + off) = h;
+      if (valid) vstore<ZK_K2_NT_STORE>(h, (uint64_t*)(slot + off));
     } else {
       // Realign through the neighbour lane: lane i writes the aligned 8-byte
       // word holding its last `me` results and lane i+1's first 4 - me.
@@ -397,7 +397,8 @@ __global__ __launch_bounds__(ZK_K2_THREADS) void k2_adam(
           for (uint32_t e = 0; e < 4u - me; ++e) slot[off + e] = (uint16_t)(h >> (16 * e));
         }
         if (right) {
-          *(uint64_t*)(slot + off + 4 - me) = (h >> (16 * (4u - me))) | (hn << (16 * me));
+          vstore<ZK_K2_NT_STORE>((h >> (16 * (4u - me))) | (hn << (16 * me)),
+                                 (uint64_t*)(slot + off + 4 - me));
         } else {
           for (uint32_t e = 4u - me; e < 4u; ++e) slot[off + e] = (uint16_t)(h >> (16 * e));
         }
