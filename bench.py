@@ -119,10 +119,19 @@ def main():
 
     abi.lib()
     w = synth.BY_NAME[a.workload]
-    dev = DeviceShard(w, a.rank, **({} if a.row_align is None else {"row_align": a.row_align}))
+    if w.units is not None:
+        from zero_sharded_optimizer_rank_amd.units import DeviceUnits
+        dev = DeviceUnits(w, a.rank)
+        real = dev.real_count()
+        S = dev.plan.rank_shard
+        k_names = ("k1u_reduce_check", "k2u_adam")
+    else:
+        dev = DeviceShard(w, a.rank, **({} if a.row_align is None else {"row_align": a.row_align}))
+        real = abi.zero_plan_real(dev.full_plan, a.rank)
+        S = dev.count
+        k_names = ("k1_reduce_check", "k2_adam")
     stream = dev.stream
     n = w.world_size
-    real = abi.zero_plan_real(dev.full_plan, a.rank)
     other_sq = w.other_sq(real) if w.other_ranks_from_config else 0.0
     t_setup = time.perf_counter()
     dev.load_initial_state()
@@ -154,13 +163,12 @@ def main():
     k2_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / a.steps
     ms_per_step = wall * 1e3 / a.steps
 
-    S = dev.count
     b1, b2 = bytes_per_param(n)
     kernels = {
-        "k1_reduce_check": {"ms": k1_ms, "bytes_per_param": b1, "bytes": b1 * S,
-                            "gbps": b1 * S / (k1_ms * 1e6)},
-        "k2_adam": {"ms": k2_ms, "bytes_per_param": b2, "bytes": b2 * S,
-                    "gbps": b2 * S / (k2_ms * 1e6)},
+        k_names[0]: {"ms": k1_ms, "bytes_per_param": b1, "bytes": b1 * S,
+                     "gbps": b1 * S / (k1_ms * 1e6)},
+        k_names[1]: {"ms": k2_ms, "bytes_per_param": b2, "bytes": b2 * S,
+                     "gbps": b2 * S / (k2_ms * 1e6)},
     }
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
     traffic = traffic_for(w.name, dom)
@@ -210,7 +218,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: rank {a.rank} of N={n}, shard S={S} "
-                               f"(psi={w.psi}), fp16 contributions, fp32 master/m/v",
+                               f"(psi={w.psi}), fp16 contributions, fp32 master/m/v"
+                               + (f", {dev.n_units} FSDP units" if w.units else ""),
                    "world_size_simulated": n, "shard": S, "psi": w.psi},
         "hbm_gbps_step": (2 * n + 34) * S / (ms_per_step * 1e6),
         "hbm_gbps_step_floor_bytes": (2 * n + 26) * S / (ms_per_step * 1e6),
@@ -220,7 +229,7 @@ def main():
         "setup_s": setup_s,
         "kernel_hash": kernel_hash(),
     }
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and w.units is None:
         out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
     print(json.dumps(out), flush=True)
 

@@ -234,6 +234,94 @@ int zero_reduce_adam_step(const zero_plan_t* plan, int32_t rank, const uint16_t*
                           const zero_step_args_t* args, zero_step_result_t* dev_result,
                           hipStream_t stream);
 
+/* ------------------------------------------------------------------------ */
+/* ZeRO-3 / FSDP units: each unit (a run of consecutive tensors, e.g. one
+ * transformer block) is flattened and sharded on its own, and one launch of
+ * each kernel updates every unit a rank holds.  Pages: "10.6 ZeRO 与 FSDP",
+ * §10.6.4 (stage 3: each GPU updates its 1/N of the parameters from its 1/N
+ * of the optimizer state and gradient) and §10.6.7 (FSDP units are flattened,
+ * sharded and gathered together; one unit per transformer block). */
+
+typedef struct zero_unit_plan {
+  int64_t n_units, world_size, align;
+  int64_t psi;        /* real parameters over all units */
+  int64_t rank_shard; /* elements a rank holds over all units (sum of S_u) */
+} zero_unit_plan_t;
+
+typedef struct zero_unit_info {
+  int64_t psi;         /* real parameters of the unit */
+  int64_t shard;       /* S_u = ceil(psi_u / N) rounded up to align */
+  int64_t flat_offset; /* first model element of the unit */
+  int64_t rank_offset; /* where the unit's shard starts in a rank's concatenation */
+} zero_unit_info_t;
+
+/*
+ * zero_plan_units: plan FSDP units.  unit_of_tensor[i] is tensor i's unit;
+ * units are consecutive runs numbered 0, 1, 2, ...  Unit u is flattened in
+ * list order and padded on its own to N * S_u; rank r owns [r*S_u, (r+1)*S_u)
+ * of it.  units_out: host [units_cap], caller-owned.  Pure host code.
+ * Errors: ZERO_EINVAL (NULL arguments, a negative numel, units not numbered
+ * as runs from 0, world_size or align < 1, overflow), ZERO_ENOSPC (more units
+ * than units_cap; plan_out is still filled).
+ */
+int zero_plan_units(const int64_t* numels, int32_t n_tensors, const int32_t* unit_of_tensor,
+                    int32_t world_size, int32_t align_elems, zero_unit_plan_t* plan_out,
+                    zero_unit_info_t* units_out, int32_t units_cap);
+
+/* One unit's buffers on this rank (all device pointers, all caller-owned). */
+typedef struct zero_unit_buffers {
+  const uint16_t* contrib; /* N fp16 rows: row r at contrib + r*ld; 16-byte aligned */
+  int64_t ld;              /* elements between rows: >= shard, a multiple of 8 */
+  float* grad;             /* [shard] fp32, 16-byte aligned (reduce output) */
+  float* master;           /* [shard] fp32, 16-byte aligned, in place */
+  float* m;                /* [shard] fp32, 16-byte aligned, in place */
+  float* v;                /* [shard] fp32, 16-byte aligned, in place */
+  uint16_t* param16;       /* [shard] fp16 slot of this rank's piece, 2-byte aligned */
+  int64_t shard;           /* S_u, elements (padding included) */
+  int64_t reduce_block;    /* first reduce workgroup: set by zero_units_prepare */
+  int64_t adam_block;      /* first Adam workgroup: set by zero_units_prepare */
+} zero_unit_buffers_t;
+
+/*
+ * zero_units_prepare: check a host unit table and fill reduce_block and
+ * adam_block; also return the workgroup totals.  The caller then copies the
+ * table to device memory and passes both copies to the calls below (the
+ * device copy must equal the prepared host copy).
+ * Errors: ZERO_EINVAL (n_units < 0, NULL pointers, a shard outside
+ * 0..ZERO_MAX_SHARD, ld < shard or not a multiple of 8, grid too large),
+ * ZERO_EALIGN (alignment as stated in zero_unit_buffers_t).
+ */
+int zero_units_prepare(zero_unit_buffers_t* units, int32_t n_units, int64_t* reduce_blocks_out,
+                       int64_t* adam_blocks_out);
+
+/* Workspace bytes for a prepared table: 256 + 16 * (256 + reduce workgroups).
+ * Zero-fill once; every call leaves it ready for the next.  0 on bad input. */
+size_t zero_units_workspace_bytes(const zero_unit_buffers_t* units, int32_t n_units);
+
+/*
+ * zero_units_reduce_check / zero_units_adam_apply / zero_units_step: the
+ * flat calls' semantics over all units at once: one squared-norm integer, one
+ * overflow flag, one clip coefficient and one skip decision for the rank.
+ *   world_size  N (1..ZERO_MAX_RANKS): rows per unit
+ *   units_host  host copy of the prepared table (checked, not read by kernels)
+ *   units_dev   device copy of the same table (read by the kernels)
+ *   workspace, dev_result, args, stream: as in the flat calls
+ * Errors: as the flat calls, plus ZERO_EINVAL when units_host was not
+ * prepared.  Nothing is launched when a check fails.
+ */
+int zero_units_reduce_check(int32_t world_size, const zero_unit_buffers_t* units_host,
+                            const zero_unit_buffers_t* units_dev, int32_t n_units,
+                            const zero_step_args_t* args, void* workspace, size_t ws_bytes,
+                            zero_step_result_t* dev_result, hipStream_t stream);
+int zero_units_adam_apply(const zero_unit_buffers_t* units_host,
+                          const zero_unit_buffers_t* units_dev, int32_t n_units,
+                          const zero_step_args_t* args, const zero_step_result_t* dev_result,
+                          hipStream_t stream);
+int zero_units_step(int32_t world_size, const zero_unit_buffers_t* units_host,
+                    const zero_unit_buffers_t* units_dev, int32_t n_units,
+                    const zero_step_args_t* args, void* workspace, size_t ws_bytes,
+                    zero_step_result_t* dev_result, hipStream_t stream);
+
 typedef struct zero_scaler {
   double scale;            /* current loss scale */
   double growth, backoff;  /* e.g. 2.0 and 0.5 */

@@ -19,6 +19,7 @@ other than itself (printed numbers, closed forms, a library routine, brute
 force); see tests/test_oracle_*.py.  No function is parity-unpinned.
 """
 from .zero_oracle import (  # noqa: F401
-    FinalizeResult, Plan, Scalars, adam_apply, exact_sq_units, finalize, nonfinite, plan,
-    reduce_contributions, scaler_update, segments, shard_step, state_bytes, step_scalars, unscale,
+    FinalizeResult, Plan, Scalars, UnitPlan, adam_apply, exact_sq_units, finalize, nonfinite,
+    plan, plan_units, reduce_contributions, scaler_update, segments, shard_step, state_bytes,
+    step_scalars, unit_model_index, unit_shard_index, unscale,
 )

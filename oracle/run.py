@@ -94,3 +94,59 @@ def run_all_ranks(w: synth.Workload, ranks: Sequence[int] | None = None, steps: 
                                   {r: gs[r] for r in ranks}, {r: state[r] for r in ranks}))
         scale, good = scaler_update(scale, good, skipped)
     return records
+
+
+# --------------------------------------------------------------------------
+# FSDP / ZeRO-3 unit layouts.
+def workload_unit_plan(w: synth.Workload, align: int = 1):
+    from .zero_oracle import plan_units
+    return plan_units(w.numels, w.units, w.world_size, align)
+
+
+def _runs(idx: np.ndarray):
+    """Split model indexes (-1 = padding) into runs (pos, start, length) of
+    consecutive real indexes."""
+    real = idx >= 0
+    if not real.any():
+        return []
+    # a run starts at a real index whose predecessor is not the index minus one
+    prev = np.concatenate(([-2], idx[:-1]))
+    starts = np.flatnonzero(real & (idx != prev + 1))
+    ends = np.flatnonzero(real & np.concatenate((idx[1:] != idx[:-1] + 1, [True])))
+    return [(int(a), int(idx[a]), int(b - a + 1)) for a, b in zip(starts, ends)]
+
+
+def gather_contrib(w: synth.Workload, step: int, q: int, idx: np.ndarray, loss_scale: float,
+                   out: np.ndarray | None = None) -> np.ndarray:
+    """Rank q's scaled fp16 gradient at model indexes idx (-1: padding, +0)."""
+    out = np.zeros(idx.size, dtype=np.uint16) if out is None else out
+    out[:] = 0
+    for pos, start, length in _runs(idx):
+        synth.contributions(w, step, q, start, length, loss_scale, out=out[pos:pos + length])
+    return out
+
+
+def unit_rank_contrib(w: synth.Workload, up, rank: int, step: int, loss_scale: float,
+                      begin: int = 0, count: int | None = None) -> np.ndarray:
+    """[N, count] contributions for elements [begin, begin+count) of rank's
+    concatenated unit shards."""
+    from .zero_oracle import unit_shard_index
+    idx = unit_shard_index(up, rank)
+    count = idx.size - begin if count is None else count
+    idx = idx[begin:begin + count]
+    out = np.empty((w.world_size, count), dtype=np.uint16)
+    for q in range(w.world_size):
+        gather_contrib(w, step, q, idx, loss_scale, out=out[q])
+    return out
+
+
+def unit_rank_initial_state(w: synth.Workload, up, rank: int):
+    """Initial master (+0 on padding), m, v and fp16 copy of rank's
+    concatenated unit shards."""
+    from .zero_oracle import unit_shard_index
+    idx = unit_shard_index(up, rank)
+    master = np.zeros(idx.size, dtype=np.float32)
+    for pos, start, length in _runs(idx):
+        synth.masters(w, start, length, out=master[pos:pos + length])
+    z = np.zeros_like(master)
+    return master, z, z.copy(), master.astype(np.float16)

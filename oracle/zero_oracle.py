@@ -286,3 +286,76 @@ def shard_step(contrib: np.ndarray, p: np.ndarray, m: np.ndarray, v: np.ndarray,
         return StepOut(g, fin, p, m, v, h)
     p2, m2, v2, h2 = adam_apply(g, p, m, v, sc, fin.coef)
     return StepOut(g, fin, p2, m2, v2, h2)
+
+
+# --------------------------------------------------------------------------
+# FSDP / ZeRO-3 units.
+#
+# Pages: "10.6 ZeRO 与 FSDP" §10.6.4 (stage 3: each GPU updates its 1/N of
+# the parameters with its 1/N of the optimizer state and of the gradient) and
+# §10.6.7 (FSDP units: the parameters of one unit, e.g. one transformer block,
+# are flattened, sharded and gathered together).  Reading: each unit is a run
+# of consecutive tensors; it is flattened in list order and padded on its own
+# to N * S_u with S_u = ceil(psi_u / N) rounded up to `align`; rank r owns
+# [r*S_u, (r+1)*S_u) of every unit; a rank's state is its unit shards
+# concatenated in unit order.
+class UnitPlan(NamedTuple):
+    world_size: int
+    align: int
+    psi: int
+    unit_psi: Tuple[int, ...]
+    unit_shard: Tuple[int, ...]
+    unit_flat: Tuple[int, ...]  # first model element of each unit
+    unit_rank_offset: Tuple[int, ...]  # offset of each unit's shard in a rank's concatenation
+    rank_shard: int  # elements each rank holds over all units
+
+
+def plan_units(numels: Sequence[int], unit_of_tensor: Sequence[int], world_size: int,
+               align: int = 1) -> UnitPlan:
+    if len(numels) != len(unit_of_tensor) or world_size < 1 or align < 1:
+        raise ValueError("bad arguments")
+    if any(b < a for a, b in zip(unit_of_tensor, unit_of_tensor[1:])) or \
+            (unit_of_tensor and unit_of_tensor[0] != 0) or \
+            any(b - a > 1 for a, b in zip(unit_of_tensor, unit_of_tensor[1:])):
+        raise ValueError("units must be consecutive runs numbered 0, 1, 2, ...")
+    n_units = (unit_of_tensor[-1] + 1) if unit_of_tensor else 0
+    psi_u = [0] * n_units
+    for n, u in zip(numels, unit_of_tensor):
+        if n < 0:
+            raise ValueError("negative numel")
+        psi_u[u] += int(n)
+    shard_u, flat_u, roff_u = [], [], []
+    flat = roff = 0
+    for p in psi_u:
+        s = -(-(-(-p // world_size)) // align) * align
+        shard_u.append(s)
+        flat_u.append(flat)
+        roff_u.append(roff)
+        flat += p
+        roff += s
+    return UnitPlan(world_size, align, flat, tuple(psi_u), tuple(shard_u), tuple(flat_u),
+                    tuple(roff_u), roff)
+
+
+def unit_shard_index(up: UnitPlan, rank: int) -> np.ndarray:
+    """For each element of rank's concatenated unit shards, the model flat
+    index it holds, or -1 for padding."""
+    out = np.full(up.rank_shard, -1, dtype=np.int64)
+    for u in range(len(up.unit_psi)):
+        s, a = up.unit_shard[u], up.unit_rank_offset[u]
+        local = np.arange(s, dtype=np.int64) + rank * s  # index inside the unit's flat buffer
+        ok = local < up.unit_psi[u]
+        out[a:a + s][ok] = up.unit_flat[u] + local[ok]
+    return out
+
+
+def unit_model_index(up: UnitPlan, rank: int, pos: np.ndarray) -> np.ndarray:
+    """Model flat index held at positions `pos` of rank's concatenated unit
+    shards (-1 for padding); the same map as unit_shard_index, pointwise."""
+    pos = np.asarray(pos, dtype=np.int64)
+    offs = np.asarray(up.unit_rank_offset, dtype=np.int64)
+    u = np.searchsorted(offs, pos, side="right") - 1
+    shard = np.asarray(up.unit_shard, dtype=np.int64)[u]
+    local = pos - offs[u] + rank * shard
+    real = local < np.asarray(up.unit_psi, dtype=np.int64)[u]
+    return np.where(real, np.asarray(up.unit_flat, dtype=np.int64)[u] + local, -1)

@@ -19,8 +19,8 @@ from typing import Optional, Tuple
 import numpy as np
 
 from .workloads import (  # noqa: F401
-    ALL, BY_NAME, FLAT75, GPT2, LLAMA2_70B, LLAMA3_8B, PURPOSE_CONTRIB, PURPOSE_INJECT,
-    PURPOSE_MASTER, TINY, Workload,
+    ALL, BY_NAME, FLAT75, GPT2, GPT2_FSDP, LLAMA2_70B, LLAMA3_8B, LLAMA3_8B_FSDP,
+    PURPOSE_CONTRIB, PURPOSE_INJECT, PURPOSE_MASTER, TINY, TINY_FSDP, UNIT_WORKLOADS, Workload,
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

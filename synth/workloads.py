@@ -90,6 +90,7 @@ class Workload:
     master_sigma: float = 0.02
     other_ranks_from_config: bool = False  # stand in the other ranks' squared norm by a constant
     parity_ranks: Tuple[int, ...] = field(default=(0,))
+    units: Optional[Tuple[int, ...]] = None  # FSDP unit of each tensor (None: one flat buffer)
 
     @property
     def numels(self) -> Tuple[int, ...]:
@@ -137,4 +138,45 @@ LLAMA2_70B = Workload(
 )
 
 ALL = (TINY, GPT2, FLAT75, LLAMA3_8B, LLAMA2_70B)
-BY_NAME = {w.name: w for w in ALL}
+
+
+# ZeRO-3 / FSDP layouts: the same tensor lists wrapped into units, one per
+# transformer block, with the embeddings and the final norm / head as units of
+# their own.  Each unit is flattened and sharded over N separately.
+def _units_by_prefix(tensors, first_prefixes, last_prefixes):
+    units, u = [], 0
+    block = None
+    for name, _ in tensors:
+        if any(name.startswith(p) for p in first_prefixes):
+            units.append(0)
+            continue
+        if any(name.startswith(p) for p in last_prefixes):
+            units.append(u + 1)
+            continue
+        b = name.split(".")[0]
+        if b != block:
+            block = b
+            u += 1
+        units.append(u)
+    return tuple(units)
+
+
+TINY_FSDP = Workload(
+    name="tiny_fsdp", cfg_id=11, tensors=_tiny(), world_size=4, sigma=1e-2, loss_scale0=1024.0,
+    lr=1e-3, weight_decay=0.0, max_grad_norm=0.0, steps=3, parity_ranks=(0, 1, 2, 3),
+    units=(0, 1, 2),
+)
+GPT2_FSDP = Workload(
+    name="gpt2_1p5b_fsdp", cfg_id=12, tensors=_gpt2_1p5b(), world_size=64, sigma=1e-3,
+    loss_scale0=65536.0, lr=1.5e-4, weight_decay=0.01, max_grad_norm=0.0, steps=5,
+    parity_ranks=(0, 1, 63), units=_units_by_prefix(_gpt2_1p5b(), ("wte", "wpe"), ("ln_f",)),
+)
+LLAMA3_8B_FSDP = Workload(
+    name="llama3_8b_fsdp", cfg_id=14, tensors=_llama(4096, 1024, 14336, 128256, 32), world_size=8,
+    sigma=1e-3, loss_scale0=65536.0, lr=3e-4, weight_decay=0.1, max_grad_norm=1.0, steps=4,
+    other_ranks_from_config=True, parity_ranks=(0, 1, 7),
+    units=_units_by_prefix(_llama(4096, 1024, 14336, 128256, 32), ("embed",),
+                           ("final_norm", "lm_head")),
+)
+UNIT_WORKLOADS = (TINY_FSDP, GPT2_FSDP, LLAMA3_8B_FSDP)
+BY_NAME = {w.name: w for w in ALL + UNIT_WORKLOADS}

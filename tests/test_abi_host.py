@@ -106,3 +106,66 @@ def test_host_argument_errors():
         assert abi.zero_workspace_bytes(p) == 256 + 16 * (256 + max(1, -(-groups // 256)))
     assert abi.zero_workspace_bytes(abi.zero_plan_t(0, 1, 1, -1, -1)) == 0
     assert abi.RESULT_BYTES == 56
+
+
+def test_plan_units_matches_oracle():
+    abi = _abi()
+    rnd = random.Random(9)
+    for _ in range(300):
+        t = rnd.randint(1, 8)
+        numels = [rnd.randint(0, 40) for _ in range(t)]
+        units, u = [], 0
+        for i in range(t):
+            if i > 0 and rnd.random() < 0.5:
+                u += 1
+            units.append(u)
+        n = rnd.randint(1, 17)
+        align = rnd.choice([1, 2, 8])
+        plan, infos = abi.zero_plan_units(numels, units, n, align)
+        want = oracle.plan_units(numels, units, n, align)
+        assert (plan.n_units, plan.psi, plan.rank_shard) == (len(want.unit_psi), want.psi,
+                                                               want.rank_shard)
+        got = [(i.psi, i.shard, i.flat_offset, i.rank_offset) for i in infos]
+        assert got == list(zip(want.unit_psi, want.unit_shard, want.unit_flat,
+                               want.unit_rank_offset))
+    for w in synth.UNIT_WORKLOADS:
+        plan, infos = abi.zero_plan_units(w.numels, w.units, w.world_size)
+        want = oracle.plan_units(w.numels, w.units, w.world_size)
+        assert plan.rank_shard == want.rank_shard and len(infos) == len(want.unit_psi)
+    with pytest.raises(abi.ZeroError):
+        abi.zero_plan_units([1, 2], [0, 2], 2)  # units must be runs 0, 1, 2, ...
+    with pytest.raises(abi.ZeroError):
+        abi.zero_plan_units([1, 2], [1, 1], 2)
+
+
+def test_units_prepare_layout_and_errors():
+    abi = _abi()
+    shards = [0, 5, 2048, 4096 * 3 + 1, 7]
+    tab = abi.unit_table(len(shards))
+    base = 1 << 40  # fake, aligned device addresses: nothing is launched here
+    for i, s in enumerate(shards):
+        t = tab[i]
+        t.contrib = t.grad = t.master = t.m = t.v = base + i * (1 << 32)
+        t.param16 = base + i * (1 << 32) + 6  # any 2-byte alignment is allowed
+        t.ld = -(-max(s, 1) // 8) * 8
+        t.shard = s
+    b1, b2 = abi.zero_units_prepare(tab, len(shards))
+    k1 = [max(1, -(-(-(-s // 4)) // 512)) for s in shards]
+    k2 = [-(-(-(-s // 4)) // 64) if s else 0 for s in shards]
+    assert b1 == sum(k1) and b2 == sum(k2)
+    assert [tab[i].reduce_block for i in range(len(shards))] == [sum(k1[:i]) for i in range(5)]
+    assert [tab[i].adam_block for i in range(len(shards))] == [sum(k2[:i]) for i in range(5)]
+    assert abi.zero_units_workspace_bytes(tab, len(shards)) == 256 + 16 * (256 + b1)
+    tab[2].grad += 4
+    with pytest.raises(abi.ZeroError) as e:
+        abi.zero_units_prepare(tab, len(shards))
+    assert e.value.code == abi.ZERO_EALIGN
+    tab[2].grad -= 4
+    tab[3].ld = tab[3].shard - 1
+    with pytest.raises(abi.ZeroError) as e:
+        abi.zero_units_prepare(tab, len(shards))
+    assert e.value.code == abi.ZERO_EINVAL
+    tab[3].ld = -(-tab[3].shard // 8) * 8
+    abi.zero_units_prepare(tab, len(shards))
+    tab[4].adam_block += 1  # a stale table is refused
+    assert abi.zero_units_workspace_bytes(tab, len(shards)) == 0

@@ -1,0 +1,182 @@
+"""GPU parity of the FSDP / ZeRO-3 unit path (zero_units_*): every unit a rank
+holds is updated by one launch of each kernel, against the oracle on the same
+seeded inputs."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import fast
+from oracle import run as orun
+
+from parity_util import check_result, compare_state, StepReport
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _bits(a):
+    return a.view(np.uint32 if a.dtype == np.float32 else np.uint16)
+
+
+@pytest.mark.parametrize("variant", ["config", "clipped", "skip"])
+def test_tiny_fsdp_all_ranks(variant):
+    """All four ranks of the tiny unit layout (units of 1e6, 1000 and 3
+    elements, the last padded), three steps, with the exact all-reduce of the
+    squared-norm integers and overflow flags between the ranks."""
+    import zero_sharded_optimizer_rank_amd.abi as abi
+    from zero_sharded_optimizer_rank_amd.units import DeviceUnits
+
+    print(f"[tiny_fsdp {variant}]", flush=True)
+    w = synth.TINY_FSDP
+    max_norm = 1.0 if variant == "clipped" else w.max_grad_norm
+    if variant == "skip":
+        w = dataclasses.replace(w, inject_step=2)
+    n = w.world_size
+    up = orun.workload_unit_plan(w)
+    devs = [DeviceUnits(w, r) for r in range(n)]
+    for d in devs:
+        d.load_initial_state()
+    ost = [list(orun.unit_rank_initial_state(w, up, r)) for r in range(n)]
+    ost = [[s[0], s[1], s[2], s[3].view(np.uint16)] for s in ost]
+    scaler = abi.new_scaler(w.loss_scale0)
+    o_scale, o_good, o_t = w.loss_scale0, 0, 0
+    flat_plan = abi.zero_plan_t(0, n, 1, 0, 0)
+    for step in range(1, w.steps + 1):
+        for d in devs:
+            d.load_contributions(step, scaler.scale)
+        base = devs[0].args(scaler.t + 1, scaler.scale, max_norm=max_norm)
+        for d in devs:
+            d.reduce_check(base)
+        rs = [d.result() for d in devs]
+        for r, d in enumerate(devs):
+            a = d.args(scaler.t + 1, scaler.scale, max_norm=max_norm,
+                       other_q=sum(rs[x].own_q for x in range(n) if x != r),
+                       other_overflow=any(rs[x].overflow for x in range(n) if x != r))
+            abi.zero_finalize(flat_plan, a, d.res, d.stream)
+            d.adam_apply(a)
+        # oracle
+        sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, o_t + 1, n, o_scale)
+        accs = [oracle.reduce_contributions(orun.unit_rank_contrib(w, up, r, step, o_scale))
+                for r in range(n)]
+        qs = [oracle.exact_sq_units(x) for x in accs]
+        bads = [oracle.nonfinite(x) for x in accs]
+        skipped = None
+        for r, d in enumerate(devs):
+            fin = oracle.finalize(qs[r], bads[r], sc.inv64, max_norm,
+                                  other_q=sum(qs) - qs[r],
+                                  other_overflow=any(bads[x] for x in range(n) if x != r))
+            res = d.result()
+            check_result(res, fin, step)
+            skipped = fin.skip
+            g = oracle.unscale(accs[r], sc.inv32)
+            assert np.array_equal(_bits(d.fetch("grad")), _bits(g)), (step, r)
+            if not fin.skip:
+                p, m, v, h = oracle.adam_apply(g, ost[r][0], ost[r][1], ost[r][2], sc, fin.coef)
+                ost[r] = [p, m, v, h.view(np.uint16)]
+            rep = StepReport(step, fin.skip, float(fin.coef))
+            for name, k in (("master", 0), ("m", 1), ("v", 2), ("slot", 3)):
+                compare_state(rep, name, d.fetch(name), ost[r][k])
+            assert all(x == 0 for x in rep.mismatches.values()), (step, r, rep.mismatches)
+            assert d.guards_intact()
+        if variant == "clipped":
+            assert fin.coef < 1
+        if variant == "skip":
+            assert skipped == (step == 2)
+        abi.zero_scaler_update(scaler, skipped)
+        o_scale, o_good = oracle.scaler_update(o_scale, o_good, skipped)
+        o_t += 0 if skipped else 1
+
+
+def _feed_units_and_reduce(dev, step, scale, pos):
+    """Generate each unit's contributions chunk by chunk, copy them to the
+    unit's rows and reduce the same host chunks with the C oracle.  Returns
+    (Q, overflow, contributions at the sampled positions)."""
+    w, n = dev.w, dev.w.world_size
+    chunk = (1 << 27) // n
+    host = torch.empty((n, chunk), dtype=torch.int16, pin_memory=True)
+    hnp = host.numpy().view(np.uint16)
+    q_total, bad = 0, False
+    cols = np.zeros((n, pos.size), dtype=np.uint16)
+    pu, pj = dev.locate(pos)
+    for u, b in enumerate(dev.bufs):
+        real, start = dev.unit_real(u), dev.unit_model_start(u)
+        for c0 in range(0, real, chunk):
+            k = min(chunk, real - c0)
+            for q in range(n):
+                synth.contributions(w, step, q, start + c0, k, scale, out=hnp[q, :k])
+            with torch.cuda.stream(dev.stream):
+                for q in range(n):
+                    b["contrib"][q, c0:c0 + k].copy_(host[q, :k], non_blocking=True)
+            qc, bc = fast.reduce_stats(hnp, k)
+            q_total += qc
+            bad |= bc
+            sel = (pu == u) & (pj >= c0) & (pj < c0 + k)
+            cols[:, sel] = hnp[:, pj[sel] - c0]
+            dev.stream.synchronize()
+    return q_total, bad, cols
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("w,rank", [pytest.param(synth.LLAMA3_8B_FSDP, 0, id="llama3_8b_fsdp-r0"),
+                                    pytest.param(synth.GPT2_FSDP, 1, id="gpt2_1p5b_fsdp-r1")])
+def test_units_full_rank(w, rank):
+    """A whole rank of a many-unit layout (34 units for Llama-3-8B, 50 for
+    GPT-2), every step: whole-rank Q, norm, coef and skip from the C oracle on
+    the same host chunks, and ~4k sampled elements bit for bit."""
+    import zero_sharded_optimizer_rank_amd.abi as abi
+    from zero_sharded_optimizer_rank_amd.units import DeviceUnits
+
+    print(f"[units full rank {w.name} rank {rank}]", flush=True)
+    dev = DeviceUnits(w, rank)
+    dev.load_initial_state()
+    up = orun.workload_unit_plan(w)
+    assert dev.plan.rank_shard == up.rank_shard
+    rng = np.random.default_rng(rank + 100)
+    offs = np.array(up.unit_rank_offset)
+    pos = np.unique(np.concatenate([rng.integers(0, up.rank_shard, 4096), offs,
+                                    np.minimum(offs + 3, up.rank_shard - 1),
+                                    np.arange(up.rank_shard - 16, up.rank_shard)]))
+    e = oracle.unit_model_index(up, rank, pos)
+    op = np.array([synth.masters(w, int(x), 1)[0] if x >= 0 else 0.0 for x in e],
+                  dtype=np.float32)
+    om, ov = np.zeros_like(op), np.zeros_like(op)
+    oh = op.astype(np.float16).view(np.uint16)
+    real = dev.real_count()
+    other_sq = w.other_sq(real) if w.other_ranks_from_config else 0.0
+    scaler = abi.new_scaler(w.loss_scale0)
+    o_scale, o_good, o_t = w.loss_scale0, 0, 0
+    for step in range(1, w.steps + 1):
+        q_all, bad_all, cols = _feed_units_and_reduce(dev, step, scaler.scale, pos)
+        dev.step(dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq))
+        res = dev.result()
+        sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, o_t + 1, w.world_size,
+                                 o_scale)
+        fin = oracle.finalize(q_all, bad_all, sc.inv64, w.max_grad_norm, other_sq=other_sq)
+        check_result(res, fin, step)
+        acc = oracle.reduce_contributions(cols)
+        g = oracle.unscale(acc, sc.inv32)
+        assert np.array_equal(_bits(dev.fetch_at("grad", pos)), _bits(g)), step
+        if not fin.skip:
+            op, om, ov, h = oracle.adam_apply(g, op, om, ov, sc, fin.coef)
+            oh = h.view(np.uint16)
+        rep = StepReport(step, fin.skip, float(fin.coef))
+        for name, want in (("master", op), ("m", om), ("v", ov), ("slot", oh)):
+            compare_state(rep, name, dev.fetch_at(name, pos), want)
+        assert all(x == 0 for x in rep.mismatches.values()), (step, rep.mismatches)
+        assert dev.guards_intact()
+        print(f"  step {step}: coef={float(fin.coef):.6g} norm={fin.norm:.6g}", flush=True)
+        abi.zero_scaler_update(scaler, bool(res.skip))
+        o_scale, o_good = oracle.scaler_update(o_scale, o_good, fin.skip)
+        o_t += 0 if fin.skip else 1
+    del dev
+    torch.cuda.empty_cache()

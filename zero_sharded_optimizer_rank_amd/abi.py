@@ -67,7 +67,26 @@ class zero_scaler_t(ctypes.Structure):
                 ("t", ctypes.c_int64)]
 
 
+class zero_unit_plan_t(ctypes.Structure):
+    _fields_ = [("n_units", ctypes.c_int64), ("world_size", ctypes.c_int64),
+                ("align", ctypes.c_int64), ("psi", ctypes.c_int64),
+                ("rank_shard", ctypes.c_int64)]
+
+
+class zero_unit_info_t(ctypes.Structure):
+    _fields_ = [("psi", ctypes.c_int64), ("shard", ctypes.c_int64),
+                ("flat_offset", ctypes.c_int64), ("rank_offset", ctypes.c_int64)]
+
+
+class zero_unit_buffers_t(ctypes.Structure):
+    _fields_ = [("contrib", ctypes.c_void_p), ("ld", ctypes.c_int64), ("grad", ctypes.c_void_p),
+                ("master", ctypes.c_void_p), ("m", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("param16", ctypes.c_void_p), ("shard", ctypes.c_int64),
+                ("reduce_block", ctypes.c_int64), ("adam_block", ctypes.c_int64)]
+
+
 RESULT_BYTES = ctypes.sizeof(zero_step_result_t)
+UNIT_BUFFERS_BYTES = ctypes.sizeof(zero_unit_buffers_t)
 
 # (name, restype, argtypes) for every symbol the header declares
 _P = ctypes.POINTER
@@ -91,6 +110,20 @@ _SIGNATURES = {
     "zero_reduce_adam_step": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _P(_vp), _vp, _vp,
                                              _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                              _P(zero_step_args_t), _vp, _vp]),
+    "zero_plan_units": (ctypes.c_int, [_P(ctypes.c_int64), ctypes.c_int32, _P(ctypes.c_int32),
+                                       ctypes.c_int32, ctypes.c_int32, _P(zero_unit_plan_t),
+                                       _P(zero_unit_info_t), ctypes.c_int32]),
+    "zero_units_prepare": (ctypes.c_int, [_P(zero_unit_buffers_t), ctypes.c_int32,
+                                          _P(ctypes.c_int64), _P(ctypes.c_int64)]),
+    "zero_units_workspace_bytes": (ctypes.c_size_t, [_P(zero_unit_buffers_t), ctypes.c_int32]),
+    "zero_units_reduce_check": (ctypes.c_int, [ctypes.c_int32, _P(zero_unit_buffers_t), _vp,
+                                               ctypes.c_int32, _P(zero_step_args_t), _vp,
+                                               ctypes.c_size_t, _vp, _vp]),
+    "zero_units_adam_apply": (ctypes.c_int, [_P(zero_unit_buffers_t), _vp, ctypes.c_int32,
+                                             _P(zero_step_args_t), _vp, _vp]),
+    "zero_units_step": (ctypes.c_int, [ctypes.c_int32, _P(zero_unit_buffers_t), _vp,
+                                       ctypes.c_int32, _P(zero_step_args_t), _vp, ctypes.c_size_t,
+                                       _vp, _vp]),
     "zero_scaler_update": (ctypes.c_int, [_P(zero_scaler_t), ctypes.c_int32]),
     "zero_last_error": (ctypes.c_char_p, []),
 }
@@ -213,6 +246,51 @@ def zero_reduce_adam_step(plan, rank, contrib, master, m, v, param16_slot, grad_
                                        _addr(master), _addr(m), _addr(v), _addr(param16_slot),
                                        _addr(grad_out), _addr(workspace), ws_bytes,
                                        ctypes.byref(args), _addr(dev_result), _stream(stream)))
+
+
+def zero_plan_units(numels: Sequence[int], unit_of_tensor: Sequence[int], world_size: int,
+                    align: int = 1):
+    n = len(numels)
+    arr = (ctypes.c_int64 * max(n, 1))(*numels)
+    uot = (ctypes.c_int32 * max(n, 1))(*unit_of_tensor)
+    plan = zero_unit_plan_t()
+    cap = max(n, 1)
+    infos = (zero_unit_info_t * cap)()
+    _check(lib().zero_plan_units(arr, n, uot, world_size, align, ctypes.byref(plan), infos, cap))
+    return plan, [infos[i] for i in range(plan.n_units)]
+
+
+def unit_table(n_units: int):
+    return (zero_unit_buffers_t * max(n_units, 1))()
+
+
+def zero_units_prepare(table, n_units: int) -> Tuple[int, int]:
+    b1, b2 = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().zero_units_prepare(table, n_units, ctypes.byref(b1), ctypes.byref(b2)))
+    return b1.value, b2.value
+
+
+def zero_units_workspace_bytes(table, n_units: int) -> int:
+    return int(lib().zero_units_workspace_bytes(table, n_units))
+
+
+def zero_units_reduce_check(world_size, table_host, table_dev, n_units, args, workspace, ws_bytes,
+                            dev_result, stream=None):
+    _check(lib().zero_units_reduce_check(world_size, table_host, _addr(table_dev), n_units,
+                                         ctypes.byref(args), _addr(workspace), ws_bytes,
+                                         _addr(dev_result), _stream(stream)))
+
+
+def zero_units_adam_apply(table_host, table_dev, n_units, args, dev_result, stream=None):
+    _check(lib().zero_units_adam_apply(table_host, _addr(table_dev), n_units, ctypes.byref(args),
+                                       _addr(dev_result), _stream(stream)))
+
+
+def zero_units_step(world_size, table_host, table_dev, n_units, args, workspace, ws_bytes,
+                    dev_result, stream=None):
+    _check(lib().zero_units_step(world_size, table_host, _addr(table_dev), n_units,
+                                 ctypes.byref(args), _addr(workspace), ws_bytes,
+                                 _addr(dev_result), _stream(stream)))
 
 
 def new_scaler(scale: float, growth: float = 2.0, backoff: float = 0.5, min_scale: float = 1.0,

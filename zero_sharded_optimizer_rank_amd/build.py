@@ -41,13 +41,16 @@ def _run(cmd):
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     kobj = os.path.join(BUILD_DIR, "zero_kernels.o")
+    uobj = os.path.join(BUILD_DIR, "zero_units.o")
     hobj = os.path.join(BUILD_DIR, "zero_host.o")
     _run([HIPCC, "-x", "hip", *COMMON, *FP_FLAGS, *DEVICE_FLAGS, "-c",
           os.path.join(CSRC, "zero_kernels.hip"), "-o", kobj])
+    _run([HIPCC, "-x", "hip", *COMMON, *FP_FLAGS, *DEVICE_FLAGS, "-c",
+          os.path.join(CSRC, "zero_units.hip"), "-o", uobj])
     _run([HIPCC, *COMMON, "-ffp-contract=off", "-c", os.path.join(CSRC, "zero_host.cpp"),
           "-o", hobj])
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, hobj, "-o", tmp])
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, uobj, hobj, "-o", tmp])
     os.replace(tmp, LIB)
     # measurement-only copy kernel, in a library of its own
     tmp = CALIB_LIB + ".tmp"

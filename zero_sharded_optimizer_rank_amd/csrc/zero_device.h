@@ -1,0 +1,398 @@
+// Device building blocks shared by the flat-shard kernels (zero_kernels.hip)
+// and the multi-unit kernels (zero_units.hip): vector types, cache-hinted
+// 16-byte access, fp16 conversion, the exact squared-norm arithmetic, the
+// 128-bit workgroup reduction, the fp64 finalize, and the per-quad bodies of
+// the reduce and of the Adam update.
+//
+// Floating point: every fp32 operation is rounded on its own (contraction is
+// off here and in the build flags); division and square root are correctly
+// rounded; denormals are kept.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zero_internal.h"
+
+#pragma clang fp contract(off)
+
+// Launch shape and cache hints (compile-time; measured on MI355X).
+#ifndef ZK_K1_QUADS
+#define ZK_K1_QUADS 1  // 4-element quads per reduce thread
+#endif
+#ifndef ZK_K2_QUADS
+#define ZK_K2_QUADS 1  // 4-element quads per Adam thread
+#endif
+#ifndef ZK_K1_THREADS
+#define ZK_K1_THREADS 512  // threads per reduce workgroup (a multiple of 64)
+#endif
+#ifndef ZK_K2_THREADS
+#define ZK_K2_THREADS 64  // threads per Adam workgroup
+#endif
+#ifndef ZK_K1_NT_LOAD
+#define ZK_K1_NT_LOAD 1
+#endif
+#ifndef ZK_K1_NT_STORE
+#define ZK_K1_NT_STORE 1
+#endif
+#ifndef ZK_K2_NT_LOAD
+#define ZK_K2_NT_LOAD 1
+#endif
+#ifndef ZK_K2_NT_STORE
+#define ZK_K2_NT_STORE 1
+#endif
+
+namespace zk {
+namespace dev {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// A 128-bit partial sum; bit 63 of hi carries the overflow flag (a workgroup
+// partial is below 2^105, so the bit is free).
+struct Partial {
+  uint64_t lo, hi;
+};
+static_assert(sizeof(Partial) == kPartialBytes, "partial layout");
+
+constexpr int kRankBatch = 8;  // contribution rows loaded before they are summed
+
+template <bool NT, typename T>
+__device__ __forceinline__ T vload(const T* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool NT, typename T>
+__device__ __forceinline__ void vstore(T v, T* p) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+__device__ __forceinline__ float h2f(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+__device__ __forceinline__ uint32_t f2h(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// acc^2 in units of 2^-48 as a 128-bit integer (lo, hi); sets bad for a
+// non-finite acc, which contributes nothing.  With m the 24-bit significand
+// and e the biased exponent, acc^2 = m^2 * 2^(2e - 300) = m^2 * 2^(2e - 252)
+// units.  Sums of fp16 values are multiples of 2^-24, so a right shift here
+// only drops zero bits.
+__device__ __forceinline__ void sq_units(float acc, uint64_t& lo, uint64_t& hi, uint32_t& bad) {
+  const uint32_t bits = __float_as_uint(acc) & 0x7FFFFFFFu;
+  const uint32_t e = bits >> 23;
+  const bool fin = e != 0xFFu;
+  bad |= fin ? 0u : 1u;
+  uint32_t mant = (bits & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+  mant = fin ? mant : 0u;
+  const int sh = 2 * (int)(e ? e : 1u) - 252;
+  const uint64_t sq = (uint64_t)mant * (uint64_t)mant;  // < 2^48
+  const uint32_t s = (uint32_t)(sh < 0 ? -sh : sh);
+  const uint64_t l_lo = s < 64 ? (sq << (s & 63)) : 0ull;
+  const uint64_t l_hi = s == 0 ? 0ull
+                        : s < 64 ? (sq >> ((64 - s) & 63))
+                        : s < 128 ? (sq << ((s - 64) & 63))
+                        : 0ull;
+  const uint64_t r_lo = s < 64 ? (sq >> (s & 63)) : 0ull;
+  lo = sh >= 0 ? l_lo : r_lo;
+  hi = sh >= 0 ? l_hi : 0ull;
+}
+
+__device__ __forceinline__ void add128(uint64_t& alo, uint64_t& ahi, uint64_t blo, uint64_t bhi) {
+  alo += blo;
+  ahi += bhi + (alo < blo ? 1ull : 0ull);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int mask) {
+  return (uint64_t)__shfl_xor((long long)x, mask);
+}
+
+__device__ __forceinline__ uint64_t shfl_down_u64(uint64_t x, unsigned int delta) {
+  const uint32_t lo = (uint32_t)__shfl_down((int)(uint32_t)x, delta);
+  const uint32_t hi = (uint32_t)__shfl_down((int)(uint32_t)(x >> 32), delta);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Sum (lo, hi, bad) over a workgroup of T threads; valid in thread 0.
+template <int T>
+__device__ void block_reduce(uint64_t& lo, uint64_t& hi, uint32_t& bad) {
+  static_assert(T % 64 == 0, "whole waves");
+  for (int off = 32; off > 0; off >>= 1) {
+    add128(lo, hi, shfl_xor_u64(lo, off), shfl_xor_u64(hi, off));
+    bad |= (uint32_t)__shfl_xor((int)bad, off);
+  }
+  if constexpr (T == 64) return;
+  __shared__ uint64_t s_lo[T / 64], s_hi[T / 64];
+  __shared__ uint32_t s_bad[T / 64];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_lo[wave] = lo;
+    s_hi[wave] = hi;
+    s_bad[wave] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < T / 64; ++w) {
+      add128(lo, hi, s_lo[w], s_hi[w]);
+      bad |= s_bad[w];
+    }
+  }
+}
+
+__device__ __forceinline__ Partial make_partial(uint64_t lo, uint64_t hi, uint32_t bad) {
+  return Partial{lo, hi | ((uint64_t)(bad ? 1u : 0u) << 63)};
+}
+
+// Round a nonnegative integer c*2^128 + hi*2^64 + lo (c in {0,1}) to the
+// nearest fp64, ties to even.
+__device__ inline double u129_to_f64(uint32_t c, uint64_t hi, uint64_t lo) {
+  if (!c && !hi) return (double)lo;  // uint64 -> fp64 rounds once
+  uint64_t top, scale_exp;
+  bool sticky;
+  if (c) {
+    top = 0x8000000000000000ull | (hi >> 1);
+    sticky = (hi & 1ull) || lo;
+    scale_exp = 65;
+  } else {
+    const int lz = __clzll((long long)hi);
+    top = lz ? ((hi << lz) | (lo >> (64 - lz))) : hi;
+    sticky = (lz ? (lo << lz) : lo) != 0;
+    scale_exp = 64 - lz;
+  }
+  uint64_t keep = top >> 11;
+  const uint64_t rb = top & 0x7FFull;
+  if (rb > 0x400ull || (rb == 0x400ull && (sticky || (keep & 1ull)))) keep += 1;
+  return __builtin_ldexp((double)keep, (int)scale_exp + 11);
+}
+
+// The norm, clip coefficient and skip decision from this rank's exact Q and
+// the other ranks' share (see zero_step_result_t in zero_shard.h).
+__device__ inline void finalize_into(uint64_t qlo, uint64_t qhi, uint32_t bad,
+                                     const FinalizeArgs& fa, zero_step_result_t* res) {
+  // (qhi:qlo) + (other_hi:other_lo) as a 129-bit value (carry:thi:tlo)
+  const uint64_t tlo = qlo + fa.other_lo;
+  const uint64_t c0 = tlo < qlo ? 1ull : 0ull;
+  const uint64_t t1 = qhi + fa.other_hi;
+  const uint64_t thi = t1 + c0;
+  const uint32_t carry = ((t1 < qhi) || (thi < t1)) ? 1u : 0u;
+  const double own = ((u129_to_f64(0, qhi, qlo) * 0x1p-48) * fa.inv64) * fa.inv64;
+  const double tot = ((u129_to_f64(carry, thi, tlo) * 0x1p-48) * fa.inv64) * fa.inv64 + fa.other_sq;
+  const double norm = __builtin_sqrt(tot);
+  double coef = 1.0;
+  if (fa.max_norm > 0.0) {
+    const double c = fa.max_norm / (norm + 1e-6);
+    coef = (c < 1.0) ? c : 1.0;
+  }
+  res->own_q_lo = qlo;
+  res->own_q_hi = qhi;
+  res->own_sq = own;
+  res->total_sq = tot;
+  res->norm = norm;
+  res->clip_coef = (float)coef;
+  res->overflow = bad ? 1 : 0;
+  res->skip = (bad || fa.other_overflow || carry) ? 1 : 0;
+  res->reserved = 0;
+}
+
+// ---------------------------------------------------------------------------
+// Reduce side, per 4-element quad: load 8 bytes from each of the n rows, sum
+// in rank order from +0, write the quad of g (16 bytes), add the exact
+// squares.  Rows gives row(r), a pointer to rank r's fp16 values.
+template <typename Rows>
+__device__ __forceinline__ void reduce_quad(const Rows& rows, int32_t n, int64_t qd, float inv32,
+                                            float* __restrict__ grad, uint64_t& qlo,
+                                            uint64_t& qhi, uint32_t& bad) {
+  const int64_t off = qd * 4;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int r0 = 0; r0 < n; r0 += kRankBatch) {
+    u32x2 d[kRankBatch];
+#pragma unroll
+    for (int b = 0; b < kRankBatch; ++b)
+      if (r0 + b < n) d[b] = vload<ZK_K1_NT_LOAD>((const u32x2*)(rows.row(r0 + b) + off));
+#pragma unroll
+    for (int b = 0; b < kRankBatch; ++b) {
+      if (r0 + b < n) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          acc[2 * w] = acc[2 * w] + h2f(d[b][w] & 0xFFFFu);
+          acc[2 * w + 1] = acc[2 * w + 1] + h2f(d[b][w] >> 16);
+        }
+      }
+    }
+  }
+  f32x4 g;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) g[e] = acc[e] * inv32;
+  vstore<ZK_K1_NT_STORE>(g, (f32x4*)(grad + off));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint64_t lo, hi;
+    sq_units(acc[e], lo, hi, bad);
+    add128(qlo, qhi, lo, hi);
+  }
+}
+
+// The last shard % 4 elements, one by one.
+template <typename Rows>
+__device__ inline void reduce_tail(const Rows& rows, int32_t n, int64_t from, int64_t shard,
+                                   float inv32, float* __restrict__ grad, uint64_t& qlo,
+                                   uint64_t& qhi, uint32_t& bad) {
+  for (int64_t j = from; j < shard; ++j) {
+    float a = 0.0f;
+    for (int r = 0; r < n; ++r) a = a + h2f(rows.row(r)[j]);
+    grad[j] = a * inv32;
+    uint64_t lo, hi;
+    sq_units(a, lo, hi, bad);
+    add128(qlo, qhi, lo, hi);
+  }
+}
+
+// Reduce kernel body for one workgroup covering quads [q_first, q_first + T*Q)
+// of a segment of `shard` elements: thread t owns quads q_first + u*T + t.
+// Returns the workgroup partial in thread 0.
+template <typename Rows>
+__device__ inline Partial reduce_block(const Rows& rows, int32_t n, int64_t shard, int64_t q_first,
+                                       float inv32, float* __restrict__ grad) {
+  uint64_t qlo = 0, qhi = 0;
+  uint32_t bad = 0;
+  const int64_t full = shard >> 2;
+#pragma unroll
+  for (int u = 0; u < ZK_K1_QUADS; ++u) {
+    const int64_t qd = q_first + (int64_t)u * ZK_K1_THREADS + threadIdx.x;
+    if (qd < full) reduce_quad(rows, n, qd, inv32, grad, qlo, qhi, bad);
+  }
+  // the thread that would own quad `full` takes the ragged tail
+  const int64_t rel = full - q_first;
+  if (rel >= 0 && rel < (int64_t)ZK_K1_THREADS * ZK_K1_QUADS &&
+      (int64_t)threadIdx.x == rel % ZK_K1_THREADS)
+    reduce_tail(rows, n, full * 4, shard, inv32, grad, qlo, qhi, bad);
+  block_reduce<ZK_K1_THREADS>(qlo, qhi, bad);
+  return make_partial(qlo, qhi, bad);
+}
+
+// ---------------------------------------------------------------------------
+// Adam, per element: one rounding per operation, in this order.
+__device__ __forceinline__ void adam1(float g, float c, const AdamScalars& sc, float& p, float& m,
+                                      float& v) {
+  const float gc = g * c;
+  m = sc.b1 * m + sc.omb1 * gc;
+  v = sc.b2 * v + sc.omb2 * (gc * gc);
+  const float den = __builtin_sqrtf(v) / sc.sqrt_bc2 + sc.eps;
+  const float u = (m / den) * sc.step_size;
+  p = p * sc.decay - u;
+}
+
+// Adam body for one wave-contiguous quad of a segment: thread's quad qd of a
+// segment with `shard` elements (full = shard / 4 whole quads).  The quads of
+// a wave must be consecutive.  The fp16 results go to slot[] with aligned
+// 8-byte stores at any slot alignment: when the slot is not 8-byte aligned,
+// lane i writes the word holding its last `me` results and lane i+1's first
+// 4 - me (through a shuffle every lane of the wave takes part in); the pieces
+// at a wave's edges or the segment's end go out as 2-byte stores.
+__device__ inline void adam_quad(const float* __restrict__ grad, float* __restrict__ master,
+                                 float* __restrict__ mom, float* __restrict__ var,
+                                 uint16_t* __restrict__ slot, int64_t shard, int64_t qd, float c,
+                                 const AdamScalars& sc) {
+  const uint32_t me = (uint32_t)(((uintptr_t)slot >> 1) & 3u);
+  const uint32_t lane = threadIdx.x & 63u;
+  const int64_t full = shard >> 2;
+  const bool valid = qd < full;
+  const int64_t off = qd * 4;
+  uint64_t h = 0;  // the quad's four fp16 results, element e in bits 16e..16e+15
+  if (valid) {
+    f32x4 g = vload<ZK_K2_NT_LOAD>((const f32x4*)(grad + off));
+    f32x4 p = vload<ZK_K2_NT_LOAD>((const f32x4*)(master + off));
+    f32x4 m = vload<ZK_K2_NT_LOAD>((const f32x4*)(mom + off));
+    f32x4 v = vload<ZK_K2_NT_LOAD>((const f32x4*)(var + off));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float pp = p[e], mm = m[e], vv = v[e];
+      adam1(g[e], c, sc, pp, mm, vv);
+      p[e] = pp;
+      m[e] = mm;
+      v[e] = vv;
+      h |= (uint64_t)f2h(pp) << (16 * e);
+    }
+    vstore<ZK_K2_NT_STORE>(p, (f32x4*)(master + off));
+    vstore<ZK_K2_NT_STORE>(m, (f32x4*)(mom + off));
+    vstore<ZK_K2_NT_STORE>(v, (f32x4*)(var + off));
+  }
+  if (me == 0) {
+    if (valid) vstore<ZK_K2_NT_STORE>(h, (uint64_t*)(slot + off));
+  } else {
+    const uint64_t hn = shfl_down_u64(h, 1);
+    const bool right = lane < 63u && qd + 1 < full;
+    if (valid) {
+      if (lane == 0u) {
+        for (uint32_t e = 0; e < 4u - me; ++e) slot[off + e] = (uint16_t)(h >> (16 * e));
+      }
+      if (right) {
+        vstore<ZK_K2_NT_STORE>((h >> (16 * (4u - me))) | (hn << (16 * me)),
+                               (uint64_t*)(slot + off + 4 - me));
+      } else {
+        for (uint32_t e = 4u - me; e < 4u; ++e) slot[off + e] = (uint16_t)(h >> (16 * e));
+      }
+    }
+  }
+  if (qd == full) {
+    // the ragged tail: the last shard % 4 elements, one by one
+    for (int64_t j = full * 4; j < shard; ++j) {
+      float pp = master[j], mm = mom[j], vv = var[j];
+      adam1(grad[j], c, sc, pp, mm, vv);
+      master[j] = pp;
+      mom[j] = mm;
+      var[j] = vv;
+      slot[j] = (uint16_t)f2h(pp);
+    }
+  }
+}
+
+// Partial-sum kernel body: sum `n_partials` partials with grid-stride
+// threads, publish one second-level partial per workgroup, and let the last
+// workgroup (ticket) sum those and finalize.  The ticket is left at zero.
+__device__ inline void reduce_partials_and_finalize(const Partial* __restrict__ partials,
+                                                    int64_t n_partials,
+                                                    Partial* __restrict__ level2,
+                                                    uint32_t* __restrict__ ticket,
+                                                    const FinalizeArgs& fa,
+                                                    zero_step_result_t* __restrict__ res) {
+  uint64_t lo = 0, hi = 0;
+  uint32_t bad = 0;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_partials;
+       i += (int64_t)gridDim.x * kThreads) {
+    const Partial pt = partials[i];
+    bad |= (uint32_t)(pt.hi >> 63);
+    add128(lo, hi, pt.lo, pt.hi & 0x7FFFFFFFFFFFFFFFull);
+  }
+  block_reduce<kThreads>(lo, hi, bad);
+  __shared__ uint32_t s_last;
+  if (threadIdx.x == 0) {
+    level2[blockIdx.x] = make_partial(lo, hi, bad);
+    __threadfence();
+    const uint32_t prev = atomicAdd(ticket, 1u);
+    s_last = (prev == gridDim.x - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  lo = hi = 0;
+  bad = 0;
+  for (uint32_t i = threadIdx.x; i < gridDim.x; i += kThreads) {
+    const Partial pt = level2[i];
+    bad |= (uint32_t)(pt.hi >> 63);
+    add128(lo, hi, pt.lo, pt.hi & 0x7FFFFFFFFFFFFFFFull);
+  }
+  block_reduce<kThreads>(lo, hi, bad);
+  if (threadIdx.x == 0) {
+    finalize_into(lo, hi, bad, fa, res);
+    *ticket = 0u;  // ready for the next call
+  }
+}
+
+}  // namespace dev
+}  // namespace zk

@@ -276,6 +276,171 @@ int zero_reduce_adam_step(const zero_plan_t* plan, int32_t rank, const uint16_t*
                          stream);
 }
 
+int zero_plan_units(const int64_t* numels, int32_t n_tensors, const int32_t* unit_of_tensor,
+                    int32_t world_size, int32_t align_elems, zero_unit_plan_t* plan_out,
+                    zero_unit_info_t* units_out, int32_t units_cap) {
+  g_err[0] = 0;
+  if (n_tensors < 0 || (n_tensors > 0 && (!numels || !unit_of_tensor)) || !plan_out ||
+      units_cap < 0 || (units_cap > 0 && !units_out))
+    return fail(ZERO_EINVAL, "NULL or negative argument");
+  if (world_size < 1 || align_elems < 1) return fail(ZERO_EINVAL, "world_size and align >= 1");
+  int64_t n_units = 0;
+  for (int32_t i = 0; i < n_tensors; ++i) {
+    const int32_t u = unit_of_tensor[i];
+    if (numels[i] < 0) return fail(ZERO_EINVAL, "numel %d is negative", i);
+    if ((i == 0 && u != 0) || (i > 0 && u != unit_of_tensor[i - 1] && u != unit_of_tensor[i - 1] + 1))
+      return fail(ZERO_EINVAL, "units must be consecutive runs numbered from 0 (tensor %d)", i);
+    n_units = (int64_t)u + 1;
+  }
+  int64_t psi = 0, roff = 0, t = 0;
+  for (int64_t u = 0; u < n_units; ++u) {
+    int64_t pu = 0;
+    for (; t < n_tensors && unit_of_tensor[t] == u; ++t) {
+      if (numels[t] > INT64_MAX / 4 - pu) return fail(ZERO_EINVAL, "unit size overflows");
+      pu += numels[t];
+    }
+    const int64_t per = pu / world_size + (pu % world_size ? 1 : 0);
+    const int64_t su = (per / align_elems + (per % align_elems ? 1 : 0)) * align_elems;
+    if (u < units_cap) {
+      units_out[u].psi = pu;
+      units_out[u].shard = su;
+      units_out[u].flat_offset = psi;
+      units_out[u].rank_offset = roff;
+    }
+    if (pu > INT64_MAX / 4 - psi || su > INT64_MAX / 4 - roff)
+      return fail(ZERO_EINVAL, "sizes overflow");
+    psi += pu;
+    roff += su;
+  }
+  plan_out->n_units = n_units;
+  plan_out->world_size = world_size;
+  plan_out->align = align_elems;
+  plan_out->psi = psi;
+  plan_out->rank_shard = roff;
+  if (n_units > units_cap) return fail(ZERO_ENOSPC, "%lld units, capacity %d", (long long)n_units, units_cap);
+  return ZERO_OK;
+}
+
+namespace {
+
+// Checks a unit table and computes each unit's first workgroups; with
+// `fill`, stores them, else compares them.
+int units_layout(zero_unit_buffers_t* units, const zero_unit_buffers_t* cunits, int32_t n_units,
+                 bool fill, int64_t* k1_total, int64_t* k2_total) {
+  if (n_units < 0 || (n_units > 0 && !cunits)) return fail(ZERO_EINVAL, "bad unit table");
+  int64_t b1 = 0, b2 = 0;
+  for (int32_t u = 0; u < n_units; ++u) {
+    const zero_unit_buffers_t& x = cunits[u];
+    if (x.shard < 0 || x.shard > ZERO_MAX_SHARD)
+      return fail(ZERO_EINVAL, "unit %d: shard outside 0..%lld", u, (long long)ZERO_MAX_SHARD);
+    if (x.shard > 0) {
+      if (!x.contrib || !x.grad || !x.master || !x.m || !x.v || !x.param16)
+        return fail(ZERO_EINVAL, "unit %d: NULL pointer", u);
+      if (x.ld < x.shard || (x.ld & 7))
+        return fail(ZERO_EINVAL, "unit %d: ld must be >= shard and a multiple of 8", u);
+      if (!aligned(x.contrib, 16) || !aligned(x.grad, 16) || !aligned(x.master, 16) ||
+          !aligned(x.m, 16) || !aligned(x.v, 16))
+        return fail(ZERO_EALIGN, "unit %d: contrib, grad, master, m, v need 16-byte alignment", u);
+      if (!aligned(x.param16, 2)) return fail(ZERO_EALIGN, "unit %d: param16 not 2-byte aligned", u);
+    }
+    const int64_t n2 = x.shard > 0 ? zk::k2_blocks(x.shard) : 0;
+    if (fill) {
+      units[u].reduce_block = b1;
+      units[u].adam_block = b2;
+    } else if (x.reduce_block != b1 || x.adam_block != b2) {
+      return fail(ZERO_EINVAL, "unit table not prepared by zero_units_prepare (unit %d)", u);
+    }
+    b1 += zk::k1_blocks(x.shard);
+    b2 += n2;
+    if (b1 > 0x7FFFFFFFll || b2 > 0x7FFFFFFFll) return fail(ZERO_EINVAL, "grid too large");
+  }
+  *k1_total = b1;
+  *k2_total = b2;
+  return ZERO_OK;
+}
+
+}  // namespace
+
+int zero_units_prepare(zero_unit_buffers_t* units, int32_t n_units, int64_t* reduce_blocks_out,
+                       int64_t* adam_blocks_out) {
+  g_err[0] = 0;
+  int64_t b1 = 0, b2 = 0;
+  const int rc = units_layout(units, units, n_units, true, &b1, &b2);
+  if (rc) return rc;
+  if (reduce_blocks_out) *reduce_blocks_out = b1;
+  if (adam_blocks_out) *adam_blocks_out = b2;
+  return ZERO_OK;
+}
+
+size_t zero_units_workspace_bytes(const zero_unit_buffers_t* units, int32_t n_units) {
+  int64_t b1 = 0, b2 = 0;
+  if (units_layout(nullptr, units, n_units, false, &b1, &b2)) return 0;
+  return zk::workspace_bytes_for_blocks(b1);
+}
+
+int zero_units_reduce_check(int32_t world_size, const zero_unit_buffers_t* units_host,
+                            const zero_unit_buffers_t* units_dev, int32_t n_units,
+                            const zero_step_args_t* args, void* workspace, size_t ws_bytes,
+                            zero_step_result_t* dev_result, hipStream_t stream) {
+  g_err[0] = 0;
+  if (world_size < 1 || world_size > ZERO_MAX_RANKS)
+    return fail(ZERO_EINVAL, "world_size outside 1..%d", ZERO_MAX_RANKS);
+  int rc = check_norm_args(args);
+  if (rc) return rc;
+  int64_t b1 = 0, b2 = 0;
+  rc = units_layout(nullptr, units_host, n_units, false, &b1, &b2);
+  if (rc) return rc;
+  if (n_units > 0 && !units_dev) return fail(ZERO_EINVAL, "units_dev is NULL");
+  if (!dev_result) return fail(ZERO_EINVAL, "dev_result is NULL");
+  if (!aligned(dev_result, 8)) return fail(ZERO_EALIGN, "dev_result not 8-byte aligned");
+  if (!workspace) return fail(ZERO_EINVAL, "workspace is NULL");
+  if (!aligned(workspace, 16)) return fail(ZERO_EALIGN, "workspace not 16-byte aligned");
+  const size_t need = zk::workspace_bytes_for_blocks(b1);
+  if (ws_bytes < need) return fail(ZERO_ENOSPC, "workspace %zu bytes < %zu", ws_bytes, need);
+  zero_plan_t pl{0, world_size, 1, 0, 0};
+  const zk::FinalizeArgs fa = finalize_args(&pl, args);
+  if (b1 > 0) {
+    rc = hip_status(zk::launch_units_reduce(units_dev, n_units, b1, world_size, (float)fa.inv64,
+                                            workspace, stream),
+                    "units reduce launch");
+    if (rc) return rc;
+  }
+  return hip_status(zk::launch_partials_finalize(workspace, b1, fa, dev_result, stream),
+                    "finalize launch");
+}
+
+int zero_units_adam_apply(const zero_unit_buffers_t* units_host,
+                          const zero_unit_buffers_t* units_dev, int32_t n_units,
+                          const zero_step_args_t* args, const zero_step_result_t* dev_result,
+                          hipStream_t stream) {
+  g_err[0] = 0;
+  int rc = check_adam_args(args);
+  if (rc) return rc;
+  int64_t b1 = 0, b2 = 0;
+  rc = units_layout(nullptr, units_host, n_units, false, &b1, &b2);
+  if (rc) return rc;
+  if (n_units > 0 && !units_dev) return fail(ZERO_EINVAL, "units_dev is NULL");
+  if (!dev_result) return fail(ZERO_EINVAL, "dev_result is NULL");
+  if (!aligned(dev_result, 8)) return fail(ZERO_EALIGN, "dev_result not 8-byte aligned");
+  if (b2 == 0) return ZERO_OK;
+  return hip_status(zk::launch_units_adam(units_dev, n_units, b2, adam_scalars(args), dev_result,
+                                          stream),
+                    "units adam launch");
+}
+
+int zero_units_step(int32_t world_size, const zero_unit_buffers_t* units_host,
+                    const zero_unit_buffers_t* units_dev, int32_t n_units,
+                    const zero_step_args_t* args, void* workspace, size_t ws_bytes,
+                    zero_step_result_t* dev_result, hipStream_t stream) {
+  g_err[0] = 0;
+  int rc = check_adam_args(args);
+  if (rc) return rc;
+  rc = zero_units_reduce_check(world_size, units_host, units_dev, n_units, args, workspace,
+                               ws_bytes, dev_result, stream);
+  if (rc) return rc;
+  return zero_units_adam_apply(units_host, units_dev, n_units, args, dev_result, stream);
+}
+
 int zero_scaler_update(zero_scaler_t* s, int32_t skipped) {
   g_err[0] = 0;
   if (!s || !(s->scale > 0.0)) return fail(ZERO_EINVAL, "NULL scaler or scale <= 0");

@@ -29,18 +29,30 @@ struct AdamScalars {
   float b1, omb1, b2, omb2, eps, step_size, sqrt_bc2, decay;
 };
 
-// Workgroups of the reduce kernel for a shard, and the workspace it needs:
-// ticket, kFinBlocks second-level partials, one partial per workgroup.
+// Workgroups of the reduce and Adam kernels for a shard, and the workspace
+// the reduce needs: ticket, kFinBlocks second-level partials, one partial per
+// reduce workgroup.
 int64_t k1_blocks(int64_t shard);
+int64_t k2_blocks(int64_t shard);
+size_t workspace_bytes_for_blocks(int64_t reduce_blocks);
 size_t workspace_bytes(int64_t shard);
 
 // Launchers: arguments already validated.  Return hipSuccess or the error.
 int launch_reduce_check(const uint16_t* const* contrib, int n, int64_t shard, float inv32,
                         float* grad, void* workspace, const FinalizeArgs& fa,
                         zero_step_result_t* res, hipStream_t stream);
+int launch_partials_finalize(void* workspace, int64_t n_partials, const FinalizeArgs& fa,
+                             zero_step_result_t* res, hipStream_t stream);
 int launch_finalize(const FinalizeArgs& fa, zero_step_result_t* res, hipStream_t stream);
 int launch_adam(const float* grad, float* master, float* m, float* v, uint16_t* slot,
                 int64_t shard, const AdamScalars& sc, const zero_step_result_t* res,
                 hipStream_t stream);
+void* workspace_partials(void* workspace);
+
+// Multi-unit forms (zero_units.hip): the unit table lives in device memory.
+int launch_units_reduce(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
+                        int n, float inv32, void* workspace, hipStream_t stream);
+int launch_units_adam(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
+                      const AdamScalars& sc, const zero_step_result_t* res, hipStream_t stream);
 
 }  // namespace zk

@@ -1,0 +1,82 @@
+// Multi-unit form of the shard step (ZeRO-3 / FSDP): one launch of the
+// reduce and one of the Adam kernel update every unit a rank holds.
+//
+// Pages: "10.6 ZeRO 与 FSDP" §10.6.4 (stage 3: each GPU updates its 1/N of
+// the parameters from its 1/N of the optimizer state and of the gradient) and
+// §10.6.7 (FSDP units: one unit's parameters are flattened and sharded
+// together, e.g. one transformer block per unit).  Each unit has its own
+// buffers, described by a zero_unit_buffers_t in a device table; workgroups
+// are dealt out unit by unit (zero_units_prepare records each unit's first
+// workgroup), so a workgroup finds its unit by a binary search and then runs
+// the same per-quad bodies as the flat kernels.  The squared norm and the
+// overflow flag cover all units together; the clip and skip are global.
+#include "zero_device.h"
+
+namespace zk {
+namespace {
+
+using namespace dev;
+
+struct StridedRows {
+  const uint16_t* base;
+  int64_t ld;
+  __device__ __forceinline__ const uint16_t* row(int r) const { return base + (int64_t)r * ld; }
+};
+
+// Largest unit index u with first(u) <= b (units with no workgroups are
+// skipped because the next unit starts at the same workgroup).
+template <typename First>
+__device__ __forceinline__ int32_t find_unit(int32_t n_units, int64_t b, First first) {
+  int32_t lo = 0, hi = n_units - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (first(mid) <= b) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(ZK_K1_THREADS) void k1u_reduce_check(
+    const zero_unit_buffers_t* __restrict__ units, int32_t n_units, int32_t n, float inv32,
+    Partial* __restrict__ partials) {
+  const int64_t b = blockIdx.x;
+  const int32_t u = find_unit(n_units, b, [&](int32_t i) { return units[i].reduce_block; });
+  const zero_unit_buffers_t& ub = units[u];
+  const StridedRows rows{ub.contrib, ub.ld};
+  const int64_t q_first = (b - ub.reduce_block) * ZK_K1_THREADS * ZK_K1_QUADS;
+  const Partial pt = reduce_block(rows, n, ub.shard, q_first, inv32, ub.grad);
+  if (threadIdx.x == 0) partials[b] = pt;
+}
+
+__global__ __launch_bounds__(ZK_K2_THREADS) void k2u_adam(
+    const zero_unit_buffers_t* __restrict__ units, int32_t n_units, AdamScalars sc,
+    const zero_step_result_t* __restrict__ res) {
+  if (res->skip) return;
+  const float c = res->clip_coef;
+  const int64_t b = blockIdx.x;
+  const int32_t u = find_unit(n_units, b, [&](int32_t i) { return units[i].adam_block; });
+  const zero_unit_buffers_t& ub = units[u];
+#pragma unroll
+  for (int k = 0; k < ZK_K2_QUADS; ++k) {
+    const int64_t qd = ((b - ub.adam_block) * ZK_K2_QUADS + k) * ZK_K2_THREADS + threadIdx.x;
+    adam_quad(ub.grad, ub.master, ub.m, ub.v, ub.param16, ub.shard, qd, c, sc);
+  }
+}
+
+}  // namespace
+
+int launch_units_reduce(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
+                        int n, float inv32, void* workspace, hipStream_t stream) {
+  hipLaunchKernelGGL(k1u_reduce_check, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), 0, stream,
+                     units_dev, n_units, n, inv32, (Partial*)workspace_partials(workspace));
+  return (int)hipGetLastError();
+}
+
+int launch_units_adam(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
+                      const AdamScalars& sc, const zero_step_result_t* res, hipStream_t stream) {
+  hipLaunchKernelGGL(k2u_adam, dim3((uint32_t)blocks), dim3(ZK_K2_THREADS), 0, stream, units_dev,
+                     n_units, sc, res);
+  return (int)hipGetLastError();
+}
+
+}  // namespace zk

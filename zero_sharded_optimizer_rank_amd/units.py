@@ -1,0 +1,178 @@
+"""One rank's FSDP / ZeRO-3 units on one GPU: per-unit device buffers, the
+unit table in device memory, seeded input feeding, and the one-launch step
+through the C ABI (zero_units_*).
+
+Each unit's buffers are separate allocations, as a real per-unit flat
+parameter would be.  The unit's fp16 slot keeps the alignment it has in the
+unit's flat fp16 buffer (rank * S_u mod 8 elements), with guard words around
+it.  Inputs come from ``synth`` by model element; the element each position
+holds follows the library's own unit plan (zero_plan_units).
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+import synth
+
+from . import abi
+from .shard import GUARD, GUARD_WORD, ROW_ALIGN, round_up
+
+CHUNK = 1 << 24
+
+
+
+class DeviceUnits:
+    def __init__(self, w: synth.Workload, rank: int, device: str = "cuda:0",
+                 stream: Optional[torch.cuda.Stream] = None):
+        assert w.units is not None
+        self.w, self.rank = w, rank
+        self.device = torch.device(device)
+        self.stream = stream or torch.cuda.current_stream(self.device)
+        self.plan, self.infos = abi.zero_plan_units(w.numels, w.units, w.world_size)
+        n = w.world_size
+        self.n_units = len(self.infos)
+        self.table = abi.unit_table(self.n_units)
+        self.bufs: List[dict] = []
+        for u, info in enumerate(self.infos):
+            s = info.shard
+            ld = round_up(max(s, 1), ROW_ALIGN)
+            mis = (rank * s) % 8
+            b = {
+                # padding columns must read +0; real columns are rewritten every step
+                "contrib": torch.zeros((n, ld), dtype=torch.int16, device=self.device),
+                "grad": torch.empty(max(s, 1), dtype=torch.float32, device=self.device),
+                "master": torch.empty(max(s, 1), dtype=torch.float32, device=self.device),
+                "m": torch.zeros(max(s, 1), dtype=torch.float32, device=self.device),
+                "v": torch.zeros(max(s, 1), dtype=torch.float32, device=self.device),
+                "slot_buf": torch.full((GUARD + 8 + s + GUARD,), GUARD_WORD, dtype=torch.int16,
+                                       device=self.device),
+                "slot_off": GUARD + mis, "shard": s, "ld": ld,
+            }
+            self.bufs.append(b)
+            t = self.table[u]
+            t.contrib = b["contrib"].data_ptr()
+            t.ld = ld
+            t.grad, t.master = b["grad"].data_ptr(), b["master"].data_ptr()
+            t.m, t.v = b["m"].data_ptr(), b["v"].data_ptr()
+            t.param16 = b["slot_buf"].data_ptr() + 2 * b["slot_off"]
+            t.shard = s
+        self.reduce_blocks, self.adam_blocks = abi.zero_units_prepare(self.table, self.n_units)
+        raw = bytes(self.table)[:abi.UNIT_BUFFERS_BYTES * self.n_units] or b"\0"
+        self.table_dev = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(self.device)
+        self.ws = torch.zeros(max(abi.zero_units_workspace_bytes(self.table, self.n_units), 16),
+                              dtype=torch.uint8, device=self.device)
+        self.res = torch.zeros(abi.RESULT_BYTES, dtype=torch.uint8, device=self.device)
+        self._pin16 = torch.empty(CHUNK, dtype=torch.int16, pin_memory=True)
+        self._pin32 = torch.empty(CHUNK, dtype=torch.float32, pin_memory=True)
+
+    # ---------------------------------------------------------------- layout
+    def unit_real(self, u: int) -> int:
+        info = self.infos[u]
+        return max(0, min(info.shard, info.psi - self.rank * info.shard))
+
+    def unit_model_start(self, u: int) -> int:
+        info = self.infos[u]
+        return info.flat_offset + self.rank * info.shard
+
+    def real_count(self) -> int:
+        return sum(self.unit_real(u) for u in range(self.n_units))
+
+    def slot(self, u: int) -> torch.Tensor:
+        b = self.bufs[u]
+        return b["slot_buf"][b["slot_off"]:b["slot_off"] + b["shard"]]
+
+    def guards_intact(self) -> bool:
+        for u, b in enumerate(self.bufs):
+            lo = b["slot_buf"][:b["slot_off"]]
+            hi = b["slot_buf"][b["slot_off"] + b["shard"]:]
+            if not (bool((lo == GUARD_WORD).all().item()) and bool((hi == GUARD_WORD).all().item())):
+                return False
+        return True
+
+    # --------------------------------------------------------------- feeding
+    def load_initial_state(self):
+        with torch.cuda.stream(self.stream):
+            for u, b in enumerate(self.bufs):
+                real, start = self.unit_real(u), self.unit_model_start(u)
+                b["master"].zero_()
+                for s0 in range(0, real, CHUNK):
+                    k = min(CHUNK, real - s0)
+                    synth.masters(self.w, start + s0, k, out=self._pin32.numpy()[:k])
+                    b["master"][s0:s0 + k].copy_(self._pin32[:k], non_blocking=True)
+                    self.stream.synchronize()
+                b["m"].zero_()
+                b["v"].zero_()
+                s = b["shard"]
+                self.slot(u).copy_(b["master"][:s].to(torch.float16).view(torch.int16))
+        self.stream.synchronize()
+
+    def load_contributions(self, step: int, loss_scale: float):
+        with torch.cuda.stream(self.stream):
+            for u, b in enumerate(self.bufs):
+                real, start = self.unit_real(u), self.unit_model_start(u)
+                for q in range(self.w.world_size):
+                    for s0 in range(0, real, CHUNK):
+                        k = min(CHUNK, real - s0)
+                        synth.contributions(self.w, step, q, start + s0, k, loss_scale,
+                                            out=self._pin16.numpy()[:k].view(np.uint16))
+                        b["contrib"][q, s0:s0 + k].copy_(self._pin16[:k], non_blocking=True)
+                        self.stream.synchronize()
+        self.stream.synchronize()
+
+    # ----------------------------------------------------------------- steps
+    def args(self, step_t: int, loss_scale: float, max_norm: Optional[float] = None,
+             other_sq: float = 0.0, other_q: int = 0, other_overflow: bool = False):
+        w = self.w
+        return abi.step_args(lr=w.lr, beta1=w.betas[0], beta2=w.betas[1], eps=w.eps,
+                             weight_decay=w.weight_decay,
+                             max_grad_norm=w.max_grad_norm if max_norm is None else max_norm,
+                             loss_scale=loss_scale, step=step_t, other_sq=other_sq,
+                             other_q=other_q, other_overflow=other_overflow)
+
+    def reduce_check(self, args):
+        abi.zero_units_reduce_check(self.w.world_size, self.table, self.table_dev, self.n_units,
+                                    args, self.ws, self.ws.numel(), self.res, self.stream)
+
+    def adam_apply(self, args):
+        abi.zero_units_adam_apply(self.table, self.table_dev, self.n_units, args, self.res,
+                                  self.stream)
+
+    def step(self, args):
+        abi.zero_units_step(self.w.world_size, self.table, self.table_dev, self.n_units, args,
+                            self.ws, self.ws.numel(), self.res, self.stream)
+
+    def result(self) -> abi.zero_step_result_t:
+        self.stream.synchronize()
+        return abi.zero_step_result_t.from_buffer_copy(self.res.cpu().numpy().tobytes())
+
+    def locate(self, pos: np.ndarray):
+        """(unit, offset inside the unit) of positions in the rank's concatenation."""
+        offs = np.array([i.rank_offset for i in self.infos], dtype=np.int64)
+        u = np.searchsorted(offs, pos, side="right") - 1
+        return u, pos - offs[u]
+
+    def fetch_at(self, name: str, pos: np.ndarray) -> np.ndarray:
+        """Values of a state array at positions of the rank's concatenation."""
+        self.stream.synchronize()
+        u, j = self.locate(np.asarray(pos, dtype=np.int64))
+        out = np.zeros(len(pos), dtype=np.uint16 if name == "slot" else np.float32)
+        for uu in np.unique(u):
+            sel = np.flatnonzero(u == uu)
+            t = self.slot(int(uu)) if name == "slot" else self.bufs[int(uu)][name]
+            vals = t[torch.as_tensor(j[sel], device=self.device)].cpu().numpy()
+            out[sel] = vals.view(np.uint16) if name == "slot" else vals
+        return out
+
+    def fetch(self, name: str) -> np.ndarray:
+        """The rank's concatenation over units (unit order) of a state array."""
+        self.stream.synchronize()
+        parts = []
+        for u, b in enumerate(self.bufs):
+            s = b["shard"]
+            t = self.slot(u) if name == "slot" else b[name][:s]
+            parts.append(t.cpu().numpy())
+        a = np.concatenate(parts) if parts else np.zeros(0)
+        return a.view(np.uint16) if name == "slot" else a
