@@ -162,8 +162,8 @@ typedef struct zero_step_result {
 
 /* Bytes of workspace zero_reduce_check needs for plan->shard elements:
  * 256 + 16 * (256 + ceil(ceil(S / 8) / 256)), about S / 128 bytes; 0 for a
- * NULL plan or a shard outside 0..ZERO_MAX_SHARD.  The workspace must be
- * zero-filled before its first use; every call leaves it ready for the next. */
+ * NULL plan or a shard outside 0..ZERO_MAX_SHARD.  The workspace needs no
+ * initialisation (the reduce kernel arms its own counter). */
 size_t zero_workspace_bytes(const zero_plan_t* plan);
 
 /*
@@ -179,7 +179,8 @@ size_t zero_workspace_bytes(const zero_plan_t* plan);
  *   args       host; loss_scale, max_grad_norm, other_* are read
  *   grad_out   device [S] fp32, 16-byte aligned: g_j = f32(acc_j * f32(inv))
  *              with acc_j = (...((+0 + c_0j) + c_1j) + ...) + c_(N-1)j in fp32
- *   workspace  device, >= zero_workspace_bytes(), 16-byte aligned, zeroed once
+ *   workspace  device, >= zero_workspace_bytes(plan), 16-byte aligned; its
+ *              content on entry does not matter
  *   dev_result device, 8-byte aligned; fully written
  * Errors: ZERO_EINVAL (N outside 1..ZERO_MAX_RANKS, bad rank, S outside
  * 0..ZERO_MAX_SHARD, NULL pointers, loss_scale <= 0, other_sq < 0 or not
@@ -295,7 +296,7 @@ int zero_units_prepare(zero_unit_buffers_t* units, int32_t n_units, int64_t* red
                        int64_t* adam_blocks_out);
 
 /* Workspace bytes for a prepared table: 256 + 16 * (256 + reduce workgroups).
- * Zero-fill once; every call leaves it ready for the next.  0 on bad input. */
+ * It needs no initialisation.  0 on bad input. */
 size_t zero_units_workspace_bytes(const zero_unit_buffers_t* units, int32_t n_units);
 
 /*

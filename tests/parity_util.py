@@ -83,7 +83,8 @@ def other_overflow_at(w: synth.Workload, step: int, flat_begin: int, count: int)
 
 
 def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Optional[int] = None,
-               fused: bool = True, strict: bool = True) -> List[StepReport]:
+               fused: bool = True, strict: bool = True,
+               ws_fill: Optional[int] = None) -> List[StepReport]:
     """Run `steps` steps of the workload on one window of rank's shard on the
     GPU and in the oracle; compare every step."""
     import zero_sharded_optimizer_rank_amd.abi as abi
@@ -105,6 +106,8 @@ def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Opti
         assert scaler.scale == o_scale
         ovf_other = other_overflow_at(w, step, flat_begin, count)
         # GPU
+        if ws_fill is not None:
+            dev.ws.fill_(ws_fill)  # the workspace needs no initialisation
         dev.load_contributions(step, scaler.scale)
         args = dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq, other_overflow=ovf_other)
         if fused:

@@ -277,3 +277,10 @@ def test_slot_offsets(begin, count):
     """Every slot alignment (flat offset mod 8) with lengths that end inside a
     quad, a wave or several waves: state and slot bit-exact, guards intact."""
     run_window(synth.TINY, 0, begin, count, steps=2)
+
+
+@pytest.mark.parametrize("fill", [0xAB, 0xFF])
+def test_workspace_content_does_not_matter(fill):
+    print(f"[workspace fill {fill:#x}]", flush=True)
+    run_window(synth.LLAMA3_8B, 0, 0, 3_000_001, steps=2, ws_fill=fill)
+    run_window(synth.LLAMA3_8B, 0, 0, 3_000_001, steps=2, fused=False, ws_fill=fill)

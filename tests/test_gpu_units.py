@@ -180,3 +180,35 @@ def test_units_full_rank(w, rank):
         o_t += 0 if fin.skip else 1
     del dev
     torch.cuda.empty_cache()
+
+
+def test_units_workspace_content_does_not_matter():
+    """Garbage in the workspace before each step changes nothing, and a rank
+    with no units at all still produces a result (Q = 0, no skip)."""
+    import zero_sharded_optimizer_rank_amd.abi as abi
+    from zero_sharded_optimizer_rank_amd.units import DeviceUnits
+
+    w = synth.TINY_FSDP
+    a = DeviceUnits(w, 2)
+    b = DeviceUnits(w, 2)
+    for d in (a, b):
+        d.load_initial_state()
+    for step in (1, 2):
+        for d, fill in ((a, None), (b, 0xCD)):
+            if fill is not None:
+                d.ws.fill_(fill)
+            d.load_contributions(step, w.loss_scale0)
+            d.step(d.args(step, w.loss_scale0, max_norm=0.5))
+        ra, rb = a.result(), b.result()
+        assert bytes(ra) == bytes(rb)
+        for name in ("grad", "master", "m", "v", "slot"):
+            assert np.array_equal(a.fetch(name), b.fetch(name)), name
+    tab = abi.unit_table(0)
+    res = torch.zeros(abi.RESULT_BYTES, dtype=torch.uint8, device="cuda")
+    ws = torch.full((abi.zero_units_workspace_bytes(tab, 0),), 0xEE, dtype=torch.uint8,
+                    device="cuda")
+    args = a.args(1, 1.0)
+    abi.zero_units_step(4, tab, 0, 0, args, ws, ws.numel(), res)
+    torch.cuda.synchronize()
+    r = abi.zero_step_result_t.from_buffer_copy(res.cpu().numpy().tobytes())
+    assert r.own_q == 0 and r.norm == 0.0 and not r.skip and r.clip_coef == 1.0

@@ -399,12 +399,12 @@ int zero_units_reduce_check(int32_t world_size, const zero_unit_buffers_t* units
   if (ws_bytes < need) return fail(ZERO_ENOSPC, "workspace %zu bytes < %zu", ws_bytes, need);
   zero_plan_t pl{0, world_size, 1, 0, 0};
   const zk::FinalizeArgs fa = finalize_args(&pl, args);
-  if (b1 > 0) {
-    rc = hip_status(zk::launch_units_reduce(units_dev, n_units, b1, world_size, (float)fa.inv64,
-                                            workspace, stream),
-                    "units reduce launch");
-    if (rc) return rc;
-  }
+  if (b1 == 0)  // no units: Q = 0, nothing overflowed
+    return hip_status(zk::launch_finalize_empty(fa, dev_result, stream), "finalize launch");
+  rc = hip_status(zk::launch_units_reduce(units_dev, n_units, b1, world_size, (float)fa.inv64,
+                                          workspace, stream),
+                  "units reduce launch");
+  if (rc) return rc;
   return hip_status(zk::launch_partials_finalize(workspace, b1, fa, dev_result, stream),
                     "finalize launch");
 }

@@ -11,7 +11,7 @@ namespace zk {
 
 constexpr int kThreads = 256;        // threads per workgroup (four 64-wide waves)
 constexpr int kFinBlocks = 256;      // most workgroups of the partial-sum kernel
-constexpr size_t kTicketBytes = 256; // ticket word, padded to keep partials aligned
+constexpr size_t kTicketBytes = 256; // ticket word (armed by the reduce kernel), padded
 constexpr size_t kPartialBytes = 16;
 
 // fp64 inputs of the norm / clip / skip decision.
@@ -44,6 +44,7 @@ int launch_reduce_check(const uint16_t* const* contrib, int n, int64_t shard, fl
 int launch_partials_finalize(void* workspace, int64_t n_partials, const FinalizeArgs& fa,
                              zero_step_result_t* res, hipStream_t stream);
 int launch_finalize(const FinalizeArgs& fa, zero_step_result_t* res, hipStream_t stream);
+int launch_finalize_empty(const FinalizeArgs& fa, zero_step_result_t* res, hipStream_t stream);
 int launch_adam(const float* grad, float* master, float* m, float* v, uint16_t* slot,
                 int64_t shard, const AdamScalars& sc, const zero_step_result_t* res,
                 hipStream_t stream);

@@ -34,7 +34,11 @@ struct ContribTable {
 __global__ __launch_bounds__(ZK_K1_THREADS) void k1_reduce_check(ContribTable ct, int32_t n,
                                                                  int64_t shard, float inv32,
                                                                  float* __restrict__ grad,
-                                                                 Partial* __restrict__ partials) {
+                                                                 Partial* __restrict__ partials,
+                                                                 uint32_t* __restrict__ ticket) {
+  // KF runs after this kernel on the same stream: arm its ticket here, so the
+  // workspace needs no initialisation by the caller.
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
   const int64_t q_first = (int64_t)blockIdx.x * ZK_K1_THREADS * ZK_K1_QUADS;
   const Partial pt = reduce_block(ct, n, shard, q_first, inv32, grad);
   if (threadIdx.x == 0) partials[blockIdx.x] = pt;
@@ -111,10 +115,20 @@ int launch_reduce_check(const uint16_t* const* contrib, int n, int64_t shard, fl
   for (int r = 0; r < ZERO_MAX_RANKS; ++r) ct.p[r] = r < n ? contrib[r] : nullptr;
   const int64_t blocks = k1_blocks(shard);
   hipLaunchKernelGGL(k1_reduce_check, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), 0, stream, ct,
-                     n, shard, inv32, grad, (Partial*)workspace_partials(workspace));
+                     n, shard, inv32, grad, (Partial*)workspace_partials(workspace),
+                     (uint32_t*)workspace);
   const int e = (int)hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_partials_finalize(workspace, blocks, fa, res, stream);
+}
+
+__global__ void k_finalize_empty(FinalizeArgs fa, zero_step_result_t* res) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) finalize_into(0ull, 0ull, 0u, fa, res);
+}
+
+int launch_finalize_empty(const FinalizeArgs& fa, zero_step_result_t* res, hipStream_t stream) {
+  hipLaunchKernelGGL(k_finalize_empty, dim3(1), dim3(64), 0, stream, fa, res);
+  return (int)hipGetLastError();
 }
 
 int launch_finalize(const FinalizeArgs& fa, zero_step_result_t* res, hipStream_t stream) {

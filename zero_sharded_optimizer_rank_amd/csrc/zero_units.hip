@@ -38,8 +38,9 @@ __device__ __forceinline__ int32_t find_unit(int32_t n_units, int64_t b, First f
 
 __global__ __launch_bounds__(ZK_K1_THREADS) void k1u_reduce_check(
     const zero_unit_buffers_t* __restrict__ units, int32_t n_units, int32_t n, float inv32,
-    Partial* __restrict__ partials) {
+    Partial* __restrict__ partials, uint32_t* __restrict__ ticket) {
   const int64_t b = blockIdx.x;
+  if (b == 0 && threadIdx.x == 0) *ticket = 0u;  // arm the finalize kernel's ticket
   const int32_t u = find_unit(n_units, b, [&](int32_t i) { return units[i].reduce_block; });
   const zero_unit_buffers_t& ub = units[u];
   const StridedRows rows{ub.contrib, ub.ld};
@@ -68,7 +69,8 @@ __global__ __launch_bounds__(ZK_K2_THREADS) void k2u_adam(
 int launch_units_reduce(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
                         int n, float inv32, void* workspace, hipStream_t stream) {
   hipLaunchKernelGGL(k1u_reduce_check, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), 0, stream,
-                     units_dev, n_units, n, inv32, (Partial*)workspace_partials(workspace));
+                     units_dev, n_units, n, inv32, (Partial*)workspace_partials(workspace),
+                     (uint32_t*)workspace);
   return (int)hipGetLastError();
 }
 
