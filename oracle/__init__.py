@@ -22,4 +22,6 @@ from .zero_oracle import (  # noqa: F401
     FinalizeResult, Plan, Scalars, UnitPlan, adam_apply, exact_sq_units, finalize, nonfinite,
     plan, plan_units, reduce_contributions, scaler_update, segments, shard_step, state_bytes,
     step_scalars, unit_model_index, unit_shard_index, unscale,
+    bf16_to_f32, f32_to_bf16, finalize_bf16, pairwise_sum_f64, reduce_contributions_bf16,
+    shard_step_bf16, sq_tree,
 )

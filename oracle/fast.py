@@ -1,5 +1,5 @@
-"""Python access to the C form of the oracle's reduce statistics (test
-infrastructure only; see oracle_c.c).  Built with gcc by ``build()``."""
+"""Python access to the C form of the oracle's reduce statistics and bf16
+norm tree (test infrastructure only; see oracle_c.c).  Built with gcc by ``build()``."""
 from __future__ import annotations
 
 import ctypes
@@ -33,6 +33,11 @@ def _lib():
                                         ctypes.POINTER(ctypes.c_uint64),
                                         ctypes.POINTER(ctypes.c_int32)]
     lib.oracle_reduce_stats.restype = ctypes.c_int
+    lib.oracle_reduce_tree_bf16.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                            ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.POINTER(ctypes.c_double),
+                                            ctypes.POINTER(ctypes.c_int32)]
+    lib.oracle_reduce_tree_bf16.restype = ctypes.c_int
     return lib
 
 
@@ -49,3 +54,23 @@ def reduce_stats(rows: np.ndarray, count: int | None = None):
     if rc != 0:
         raise ValueError("accumulator outside the exact range")
     return (int(hi.value) << 64) | int(lo.value), bool(bad.value)
+
+
+def reduce_tree_bf16(rows: np.ndarray, count: int | None = None, width: int | None = None):
+    """rows: [N, >= count] uint16 (bf16 bits).  Returns (tree, overflow): the
+    pairwise fp64 tree of the exact squares of the first `count` column sums,
+    zero-padded to `width` (default: the next power of two)."""
+    assert rows.dtype == np.uint16 and rows.ndim == 2 and rows.strides[1] == 2
+    n = rows.shape[0]
+    count = rows.shape[1] if count is None else count
+    if width is None:
+        width = 1
+        while width < count:
+            width *= 2
+    ptrs = (ctypes.c_void_p * n)(*[rows[r].ctypes.data for r in range(n)])
+    tree, bad = ctypes.c_double(), ctypes.c_int32()
+    rc = _lib().oracle_reduce_tree_bf16(ptrs, n, count, width, ctypes.byref(tree),
+                                        ctypes.byref(bad))
+    if rc != 0:
+        raise ValueError("bad width or out of memory")
+    return float(tree.value), bool(bad.value)

@@ -17,6 +17,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 static float half_to_float(uint16_t h) {
@@ -79,4 +80,47 @@ int oracle_reduce_stats(const uint16_t* const* rows, int n, int64_t count, uint6
   *q_hi = (uint64_t)(total >> 64);
   *bad_out = bad;
   return range_err ? -1 : 0;
+}
+
+/*
+ * bf16 path.  acc_j as above with bf16 inputs (bf16 -> fp32 is exact: the
+ * pattern is the top half of the fp32 one); sq_j = acc_j^2 in fp64 (exact),
+ * +0 for a non-finite acc_j, and +0 for j >= count up to `width`, a power of
+ * two >= count.  The result is the balanced pairwise tree over sq_0 ..
+ * sq_(width-1): level by level, node = left + right.  Written out with a
+ * scratch array of `width` doubles.  Returns 0, or -1 on a bad width or no
+ * memory.
+ */
+int oracle_reduce_tree_bf16(const uint16_t* const* rows, int n, int64_t count, int64_t width,
+                            double* tree, int32_t* bad_out) {
+  if (width < 1 || (width & (width - 1)) || width < count) return -1;
+  double* y = (double*)malloc((size_t)width * sizeof(double));
+  if (!y) return -1;
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t j = 0; j < width; ++j) {
+    double sq = 0.0;
+    if (j < count) {
+      float acc = 0.0f;
+      for (int r = 0; r < n; ++r) {
+        uint32_t bits = (uint32_t)rows[r][j] << 16;
+        float x;
+        memcpy(&x, &bits, 4);
+        acc = acc + x;
+      }
+      if (isfinite(acc)) {
+        sq = (double)acc * (double)acc;
+      } else {
+        bad = 1;
+      }
+    }
+    y[j] = sq;
+  }
+  /* in place, one thread: y[i] is written only after y[2i] and y[2i+1] were read */
+  for (int64_t half = width / 2; half >= 1; half /= 2)
+    for (int64_t i = 0; i < half; ++i) y[i] = y[2 * i] + y[2 * i + 1];
+  *tree = y[0];
+  *bad_out = bad;
+  free(y);
+  return 0;
 }

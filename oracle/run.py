@@ -13,7 +13,7 @@ import numpy as np
 import synth
 
 from .zero_oracle import (
-    FinalizeResult, Plan, exact_sq_units, finalize, nonfinite, plan, reduce_contributions,
+    FinalizeResult, Plan, exact_sq_units, f32_to_bf16, finalize, nonfinite, plan, reduce_contributions,
     adam_apply, scaler_update, step_scalars, unscale,
 )
 
@@ -35,12 +35,20 @@ def shard_contrib(w: synth.Workload, p: Plan, rank: int, step: int, loss_scale: 
 
 
 def initial_state(w: synth.Workload, p: Plan, rank: int, begin: int = 0, count: int | None = None):
-    """fp32 master, m = 0, v = 0 and the fp16 copy of the master for a shard range."""
+    """fp32 master, m = 0, v = 0 and the fp16 (or bf16, by the workload's
+    format) copy of the master for a shard range."""
     if count is None:
         count = p.shard - begin
     master = synth.masters(w, rank * p.shard + begin, count)
     z = np.zeros(count, np.float32)
-    return master, z, z.copy(), master.astype(np.float16)
+    return master, z, z.copy(), half_copy(w, master)
+
+
+def half_copy(w: synth.Workload, master: np.ndarray) -> np.ndarray:
+    """The slot's initial 16-bit copy of fp32 masters, as bit patterns."""
+    if w.dtype == "bf16":
+        return f32_to_bf16(master)
+    return master.astype(np.float16).view(np.uint16)
 
 
 class RankState(NamedTuple):

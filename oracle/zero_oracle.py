@@ -359,3 +359,87 @@ def unit_model_index(up: UnitPlan, rank: int, pos: np.ndarray) -> np.ndarray:
     local = pos - offs[u] + rank * shard
     real = local < np.asarray(up.unit_psi, dtype=np.int64)[u]
     return np.where(real, np.asarray(up.unit_flat, dtype=np.int64)[u] + local, -1)
+
+
+# --------------------------------------------------------------------------
+# bf16 variant.
+#
+# Pages: the tutorial's §4.3 advises bf16 where the hardware supports it, as
+# the alternative to tuning fp16 loss scaling.  Reading: gradient
+# contributions and the parameter slot are bfloat16, there is no loss scaling
+# (loss scale 1), master / m / v stay fp32 and the Adam sequence is unchanged.
+# bf16 keeps fp32's exponent range, so the fp16 path's exact integer norm
+# (which needs sums that are multiples of 2^-24 below 2^22) does not apply.
+# Reading for the norm: each acc_j^2 is exact in fp64 (a 24-bit significand
+# squared has at most 48 bits, and the exponent stays in range); the shard's
+# sum is the balanced pairwise tree over element indices, zero-padded to a
+# power of two, in fp64 -- one fixed order, independent of how the work is
+# split.  Across ranks the other ranks' share arrives as a plain fp64 value.
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns to fp32 (exact: bf16 is the top half of fp32)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(F32)
+
+
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    """fp32 to bfloat16 bit patterns, round to nearest even; NaN stays a quiet
+    NaN with its sign."""
+    u = np.asarray(x, dtype=F32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    nan = np.isnan(np.asarray(x, dtype=F32))
+    out = np.where(nan, (u >> 16) | 0x40, rounded)
+    return out.astype(np.uint16)
+
+
+def reduce_contributions_bf16(contrib: np.ndarray) -> np.ndarray:
+    """contrib: [N, S] bf16 bit patterns.  acc = fp32 sum in rank order from +0."""
+    assert contrib.dtype == np.uint16 and contrib.ndim == 2
+    acc = np.zeros(contrib.shape[1], dtype=F32)
+    for r in range(contrib.shape[0]):
+        acc = acc + bf16_to_f32(contrib[r])
+    return acc
+
+
+def pairwise_sum_f64(x: np.ndarray) -> float:
+    """Balanced pairwise sum in fp64: pad with +0 to a power of two, then add
+    neighbours level by level (node = left + right)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = 1
+    while n < x.size:
+        n *= 2
+    y = np.zeros(n, dtype=np.float64)
+    y[:x.size] = x
+    while y.size > 1:
+        y = y[0::2] + y[1::2]
+    return float(y[0])
+
+
+def sq_tree(acc: np.ndarray) -> float:
+    """The shard's squared norm of acc for the bf16 path: exact fp64 squares
+    (non-finite elements count +0), summed by pairwise_sum_f64."""
+    a = acc.astype(np.float64)
+    sq = np.where(np.isfinite(a), a * a, 0.0)
+    return pairwise_sum_f64(sq)
+
+
+def finalize_bf16(tree_sq: float, own_overflow: bool, inv64: float, max_norm: float,
+                  other_sq: float = 0.0, other_overflow: bool = False) -> FinalizeResult:
+    own_sq = (tree_sq * inv64) * inv64
+    total_sq = own_sq + other_sq
+    norm = math.sqrt(total_sq)
+    coef = min(1.0, max_norm / (norm + 1e-6)) if max_norm > 0 else 1.0
+    skip = bool(own_overflow or other_overflow)
+    return FinalizeResult(0, own_sq, total_sq, norm, F32(coef), bool(own_overflow), skip)
+
+
+def shard_step_bf16(contrib: np.ndarray, p: np.ndarray, m: np.ndarray, v: np.ndarray,
+                    h: np.ndarray, sc: Scalars, max_norm: float, other_sq: float = 0.0,
+                    other_overflow: bool = False) -> StepOut:
+    """One rank's bf16-path step; h and the returned slot are bf16 bit patterns."""
+    acc = reduce_contributions_bf16(contrib)
+    g = unscale(acc, sc.inv32)
+    fin = finalize_bf16(sq_tree(acc), nonfinite(acc), sc.inv64, max_norm, other_sq,
+                        other_overflow)
+    if fin.skip:
+        return StepOut(g, fin, p, m, v, h)
+    p2, m2, v2, _ = adam_apply(g, p, m, v, sc, fin.coef)
+    return StepOut(g, fin, p2, m2, v2, f32_to_bf16(p2))

@@ -19,9 +19,13 @@ from typing import Optional, Tuple
 import numpy as np
 
 from .workloads import (  # noqa: F401
-    ALL, BY_NAME, FLAT75, GPT2, GPT2_FSDP, LLAMA2_70B, LLAMA3_8B, LLAMA3_8B_FSDP,
-    PURPOSE_CONTRIB, PURPOSE_INJECT, PURPOSE_MASTER, TINY, TINY_FSDP, UNIT_WORKLOADS, Workload,
+    ALL, BF16_WORKLOADS, BY_NAME, FLAT75, GPT2, GPT2_FSDP, LLAMA2_70B, LLAMA3_8B,
+    LLAMA3_8B_BF16, LLAMA3_8B_FSDP, PURPOSE_CONTRIB, PURPOSE_INJECT, PURPOSE_MASTER, TINY,
+    TINY_BF16, TINY_FSDP, UNIT_WORKLOADS, Workload,
 )
+
+FORMATS = {"fp16": 0, "bf16": 1}
+PLUS_INF = {"fp16": 0x7C00, "bf16": 0x7F80}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libsynth.so")
@@ -48,8 +52,10 @@ def _lib() -> ctypes.CDLL:
     vp = ctypes.c_void_p
     lib.synth_philox4x32_10.argtypes = [vp, vp, vp]
     lib.synth_fp16_table_size.restype = i64
-    lib.synth_fp16_normal_table.argtypes = [ctypes.c_double, vp, vp, vp]
-    lib.synth_fp16_normal_table.restype = ctypes.c_int
+    lib.synth_table_size.argtypes = [ctypes.c_int]
+    lib.synth_table_size.restype = i64
+    lib.synth_normal_table.argtypes = [ctypes.c_int, ctypes.c_double, vp, vp, vp]
+    lib.synth_normal_table.restype = ctypes.c_int
     lib.synth_fp16_normal.argtypes = [u32, u32, u32, u32, i64, i64, i64, vp, vp, vp, vp]
     lib.synth_f32_normal.argtypes = [u32, u32, u32, u32, i64, i64, i64, ctypes.c_double, vp]
     lib.synth_words.argtypes = [u32, u32, u32, u32, i64, i64, vp]
@@ -70,13 +76,15 @@ def philox4x32_10(ctr, key) -> Tuple[int, int, int, int]:
 
 
 @functools.lru_cache(maxsize=16)
-def fp16_normal_table(std: float):
-    """(thresholds uint64, fp16 bit patterns uint16, guide uint32) for N(0, std^2)."""
-    n = int(_lib().synth_fp16_table_size())
+def normal_table(std: float, fmt: str = "fp16"):
+    """(thresholds uint64, bit patterns uint16, guide uint32) for N(0, std^2)
+    on the grid of fmt ("fp16" or "bf16")."""
+    f = FORMATS[fmt]
+    n = int(_lib().synth_table_size(f))
     thr = np.zeros(n, dtype=np.uint64)
     val = np.zeros(n, dtype=np.uint16)
     guide = np.zeros(65536, dtype=np.uint32)
-    rc = _lib().synth_fp16_normal_table(float(std), _ptr(thr), _ptr(val), _ptr(guide))
+    rc = _lib().synth_normal_table(f, float(std), _ptr(thr), _ptr(val), _ptr(guide))
     if rc != 0:
         raise ValueError(f"bad table std {std}")
     for a in (thr, val, guide):
@@ -84,23 +92,27 @@ def fp16_normal_table(std: float):
     return thr, val, guide
 
 
+def fp16_normal_table(std: float):
+    return normal_table(std, "fp16")
+
+
 def contributions(w: Workload, step: int, rank: int, begin: int, count: int, loss_scale: float,
                   out: Optional[np.ndarray] = None) -> np.ndarray:
-    """fp16 bit patterns of rank ``rank``'s scaled gradient at flat elements
-    [begin, begin+count) for 1-based step ``step``: N(0, (sigma*loss_scale)^2)
-    on the fp16 grid; elements at or past psi are +0 (padding).  Includes the
-    workload's injected +inf, if any, at that step."""
+    """Bit patterns (fp16 or bf16, per the workload) of rank ``rank``'s scaled
+    gradient at flat elements [begin, begin+count) for 1-based step ``step``:
+    N(0, (sigma*loss_scale)^2) on the format's grid; elements at or past psi
+    are +0 (padding).  Includes the workload's injected +inf, if any."""
     if out is None:
         out = np.empty(count, dtype=np.uint16)
     assert out.dtype == np.uint16 and out.size >= count
-    thr, val, guide = fp16_normal_table(w.sigma * loss_scale)
+    thr, val, guide = normal_table(w.sigma * loss_scale, w.dtype)
     _lib().synth_fp16_normal(w.key[0], w.key[1], rank, (PURPOSE_CONTRIB << 24) | step, begin, count,
                              w.psi, _ptr(thr), _ptr(val), _ptr(guide), _ptr(out))
     site = inject_site(w, step)
     if site is not None:
         q, e = site
         if q == rank and begin <= e < begin + count:
-            out[e - begin] = 0x7C00  # +inf
+            out[e - begin] = PLUS_INF[w.dtype]
     return out
 
 

@@ -12,8 +12,8 @@
  * (e mod 4) of the block at counter e/4, so any element range can be
  * regenerated on its own.
  *
- * Gradient contributions are fp16 values drawn from the normal distribution
- * N(0, std^2) discretised onto the fp16 grid: each finite fp16 value h gets
+ * Gradient contributions are fp16 (or bf16) values drawn from the normal
+ * distribution N(0, std^2) discretised onto the format's grid: each finite value h gets
  * the probability mass of the real interval that rounds to h under
  * round-to-nearest-even, resolved to 2^-32 (one 32-bit word per element) and
  * drawn by inversion with a guide table (Chen and Asau, 1974).  Master
@@ -69,49 +69,61 @@ static double half_bits_to_double(uint16_t h) {
   return s ? -x : x;
 }
 
-/* Number of entries: 31744 finite non-negative fp16 patterns (0x0000..0x7BFF)
- * and the same count of negative ones (0x8000..0xFBFF). */
+/* fp16: 31744 finite non-negative patterns (0x0000..0x7BFF) and as many
+ * negative ones; bf16: 32640 (0x0000..0x7F7F) and as many negative ones. */
 #define SYNTH_FP16_TABLE_N 63488
+#define SYNTH_BF16_TABLE_N 65280
 #define SYNTH_GUIDE_N 65536
 
 int64_t synth_fp16_table_size(void) { return SYNTH_FP16_TABLE_N; }
+int64_t synth_table_size(int fmt) { return fmt == 1 ? SYNTH_BF16_TABLE_N : SYNTH_FP16_TABLE_N; }
+
+static double bf16_bits_to_double(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
 
 static double normal_cdf(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
 
 /*
- * Build the inversion table for N(0, std^2) on the fp16 grid.
+ * Build the inversion table for N(0, std^2) on the grid of a 16-bit format
+ * (fmt 0: IEEE binary16, fmt 1: bfloat16).
  * thr[k] = floor(2^32 * Phi(b_k / std)), where b_k is the upper edge of the
- * round-to-nearest interval of the k-th fp16 value in ascending order
- * (-0 is its own value, just below +0).  val[k] is that fp16 bit pattern.
+ * round-to-nearest interval of the k-th finite value in ascending order
+ * (-0 is its own value, just below +0).  val[k] is that bit pattern.
  * guide[i] = smallest k with thr[k] > i * 2^16.
  * Returns 0, or -1 on bad arguments.
  */
-int synth_fp16_normal_table(double std, uint64_t* thr, uint16_t* val, uint32_t* guide) {
-  if (!(std > 0.0) || !thr || !val || !guide) return -1;
+int synth_normal_table(int fmt, double std, uint64_t* thr, uint16_t* val, uint32_t* guide) {
+  if (!(std > 0.0) || !thr || !val || !guide || (fmt != 0 && fmt != 1)) return -1;
+  double (*value)(uint16_t) = fmt == 1 ? bf16_bits_to_double : half_bits_to_double;
+  const int maxmag = fmt == 1 ? 0x7F7F : 0x7BFF; /* largest finite magnitude pattern */
+  const int64_t n = synth_table_size(fmt);
   int64_t k = 0;
-  /* negative values, ascending: 0xFBFF (-65504) ... 0x8001 (-2^-24) */
-  for (int mb = 0x7BFF; mb >= 1; --mb) {
-    double a = half_bits_to_double((uint16_t)mb);
-    double b = half_bits_to_double((uint16_t)(mb - 1));
+  /* negative values, ascending: -max ... -smallest subnormal */
+  for (int mb = maxmag; mb >= 1; --mb) {
+    double a = value((uint16_t)mb);
+    double b = value((uint16_t)(mb - 1));
     double edge = -0.5 * (a + b); /* midpoint toward zero */
     val[k] = (uint16_t)(0x8000 | mb);
-    double f = floor(normal_cdf(edge / std) * 4294967296.0);
-    thr[k++] = (uint64_t)f;
+    thr[k++] = (uint64_t)floor(normal_cdf(edge / std) * 4294967296.0);
   }
-  /* -0 takes [-2^-25, 0) */
+  /* -0 takes [-half the smallest subnormal, 0) */
   val[k] = 0x8000;
   thr[k++] = (uint64_t)floor(normal_cdf(0.0) * 4294967296.0);
-  /* +0 .. 65504 */
-  for (int b = 0; b <= 0x7BFF; ++b) {
+  /* +0 .. +max */
+  for (int b = 0; b <= maxmag; ++b) {
     val[k] = (uint16_t)b;
-    if (b == 0x7BFF) {
+    if (b == maxmag) {
       thr[k++] = 4294967296ull;
     } else {
-      double edge = 0.5 * (half_bits_to_double((uint16_t)b) + half_bits_to_double((uint16_t)(b + 1)));
+      double edge = 0.5 * (value((uint16_t)b) + value((uint16_t)(b + 1)));
       thr[k++] = (uint64_t)floor(normal_cdf(edge / std) * 4294967296.0);
     }
   }
-  if (k != SYNTH_FP16_TABLE_N) return -1;
+  if (k != n) return -1;
   /* monotone by construction of Phi; enforce against libm wobble */
   for (int64_t i = 1; i < k; ++i)
     if (thr[i] < thr[i - 1]) thr[i] = thr[i - 1];
@@ -122,6 +134,10 @@ int synth_fp16_normal_table(double std, uint64_t* thr, uint16_t* val, uint32_t* 
     guide[i] = (uint32_t)j;
   }
   return 0;
+}
+
+int synth_fp16_normal_table(double std, uint64_t* thr, uint16_t* val, uint32_t* guide) {
+  return synth_normal_table(0, std, thr, val, guide);
 }
 
 static inline uint16_t table_draw(uint32_t u, const uint64_t* thr, const uint16_t* val,

@@ -91,6 +91,7 @@ class Workload:
     other_ranks_from_config: bool = False  # stand in the other ranks' squared norm by a constant
     parity_ranks: Tuple[int, ...] = field(default=(0,))
     units: Optional[Tuple[int, ...]] = None  # FSDP unit of each tensor (None: one flat buffer)
+    dtype: str = "fp16"  # gradient contributions and parameter slot: "fp16" or "bf16"
 
     @property
     def numels(self) -> Tuple[int, ...]:
@@ -179,4 +180,18 @@ LLAMA3_8B_FSDP = Workload(
                            ("final_norm", "lm_head")),
 )
 UNIT_WORKLOADS = (TINY_FSDP, GPT2_FSDP, LLAMA3_8B_FSDP)
-BY_NAME = {w.name: w for w in ALL + UNIT_WORKLOADS}
+
+# bf16 variants: bf16 gradient contributions and parameter slot, no loss
+# scaling (loss scale 1 throughout), fp32 master / m / v as before.
+TINY_BF16 = Workload(
+    name="tiny_bf16", cfg_id=21, tensors=_tiny(), world_size=4, sigma=1e-2, loss_scale0=1.0,
+    lr=1e-3, weight_decay=0.0, max_grad_norm=0.0, steps=3, parity_ranks=(0, 1, 2, 3),
+    dtype="bf16",
+)
+LLAMA3_8B_BF16 = Workload(
+    name="llama3_8b_bf16", cfg_id=24, tensors=_llama(4096, 1024, 14336, 128256, 32), world_size=8,
+    sigma=1e-3, loss_scale0=1.0, lr=3e-4, weight_decay=0.1, max_grad_norm=1.0, steps=4,
+    inject_step=2, other_ranks_from_config=True, parity_ranks=(0, 1, 7), dtype="bf16",
+)
+BF16_WORKLOADS = (TINY_BF16, LLAMA3_8B_BF16)
+BY_NAME = {w.name: w for w in ALL + UNIT_WORKLOADS + BF16_WORKLOADS}

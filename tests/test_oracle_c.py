@@ -1,5 +1,5 @@
-"""Pin: the C form of the oracle's reduce statistics equals the numpy
-definition (and Python big integers) bit for bit."""
+"""Pin: the C form of the oracle's reduce statistics and bf16 norm tree
+equals the numpy definition (and Python big integers) bit for bit."""
 import numpy as np
 import pytest
 
@@ -40,3 +40,32 @@ def test_c_stats_subnormal_conversion():
     q, bad = fast.reduce_stats(rows)
     acc = oracle.reduce_contributions(rows)
     assert not bad and q == oracle.exact_sq_units(acc)
+
+
+@pytest.mark.parametrize("n", [1, 8, 64])
+def test_c_bf16_tree_equals_numpy(n):
+    rng = np.random.default_rng(200 + n)
+    for cols in (1, 5, 4096, 40_001):
+        x = (rng.standard_normal((n, cols)) * 10.0 ** rng.uniform(-20, 20, (n, cols)))
+        c = oracle.f32_to_bf16(x.astype(np.float32))
+        tree, bad = fast.reduce_tree_bf16(c)
+        acc = oracle.reduce_contributions_bf16(c)
+        assert tree == oracle.sq_tree(acc) and bad == oracle.nonfinite(acc)
+        # padding further with zeros leaves the tree unchanged
+        width = 1
+        while width < cols:
+            width *= 2
+        assert fast.reduce_tree_bf16(c, width=4 * width)[0] == tree
+
+
+def test_c_bf16_tree_chunks_compose():
+    # the tree of aligned power-of-two chunks, then the tree of their roots,
+    # is the tree of the whole (how the full-size tests use it)
+    rng = np.random.default_rng(9)
+    c = oracle.f32_to_bf16(rng.standard_normal((8, 10_000)).astype(np.float32))
+    whole, _ = fast.reduce_tree_bf16(c)
+    roots = [fast.reduce_tree_bf16(np.ascontiguousarray(c[:, i:i + 1024]))[0]
+             for i in range(0, 10_000, 1024)]
+    assert oracle.pairwise_sum_f64(np.array(roots)) == whole
+    c[3, 777] = 0x7F80  # +inf
+    assert fast.reduce_tree_bf16(c)[1]
