@@ -32,6 +32,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCES = ("zero_sharded_optimizer_rank_amd/csrc/zero_kernels.hip",
+                  "zero_sharded_optimizer_rank_amd/csrc/zero_units.hip",
+                  "zero_sharded_optimizer_rank_amd/csrc/zero_device.h",
                   "zero_sharded_optimizer_rank_amd/csrc/zero_internal.h")
 
 
@@ -45,8 +47,8 @@ def kernel_hash() -> str:
 
 def bytes_per_param(n: int):
     """Algorithmic bytes per shard element of each kernel on an applied step."""
-    k1 = 2 * n + 4   # read N fp16 contributions, write fp32 g
-    k2 = 16 + 14     # read g, master, m, v; write master, m, v and the fp16 slot
+    k1 = 2 * n + 4   # read N 16-bit contributions, write fp32 g
+    k2 = 16 + 14     # read g, master, m, v; write master, m, v and the 16-bit slot
     return k1, k2
 
 
@@ -75,12 +77,13 @@ def cpu_baseline(w, seconds: float):
     c = orun.shard_contrib(w, p, 0, 1, w.loss_scale0, 0, n)
     pm, m, v, h = orun.initial_state(w, p, 0, 0, n)
     other_sq = w.other_sq(p.real(0)) if w.other_ranks_from_config else 0.0
+    step_fn = oracle.shard_step_bf16 if w.dtype == "bf16" else oracle.shard_step
     reps, t0 = 0, time.perf_counter()
     t_applied = 0
     while True:
         sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, t_applied + 1,
                                  w.world_size, w.loss_scale0)
-        out = oracle.shard_step(c, pm, m, v, h, sc, w.max_grad_norm, other_sq=other_sq)
+        out = step_fn(c, pm, m, v, h, sc, w.max_grad_norm, other_sq=other_sq)
         pm, m, v, h = out.p, out.m, out.v, out.h
         t_applied += 0 if out.fin.skip else 1
         reps += 1
@@ -129,7 +132,8 @@ def main():
         dev = DeviceShard(w, a.rank, **({} if a.row_align is None else {"row_align": a.row_align}))
         real = abi.zero_plan_real(dev.full_plan, a.rank)
         S = dev.count
-        k_names = ("k1_reduce_check", "k2_adam")
+        k_names = (("k1_reduce_check_bf16", "k2_adam_bf16") if w.dtype == "bf16"
+                   else ("k1_reduce_check", "k2_adam"))
     stream = dev.stream
     n = w.world_size
     other_sq = w.other_sq(real) if w.other_ranks_from_config else 0.0
@@ -218,7 +222,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: rank {a.rank} of N={n}, shard S={S} "
-                               f"(psi={w.psi}), fp16 contributions, fp32 master/m/v"
+                               f"(psi={w.psi}), {w.dtype} contributions and slot, fp32 master/m/v"
                                + (f", {dev.n_units} FSDP units" if w.units else ""),
                    "world_size_simulated": n, "shard": S, "psi": w.psi},
         "hbm_gbps_step": (2 * n + 34) * S / (ms_per_step * 1e6),

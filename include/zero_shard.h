@@ -236,6 +236,33 @@ int zero_reduce_adam_step(const zero_plan_t* plan, int32_t rank, const uint16_t*
                           hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* bf16 variant: bfloat16 gradient contributions and parameter slot, no loss
+ * scaling needed (the tutorial's §4.3 suggests bf16 where the hardware has it,
+ * instead of tuning fp16 loss scaling); fp32 master, m, v and the Adam
+ * sequence are unchanged.  bf16 keeps fp32's exponent range, so the shard's
+ * squared norm is not the exact integer of the fp16 path but the balanced
+ * pairwise tree, in fp64, of the exact squares acc_j^2 over element indices
+ * zero-padded to a power of two: one fixed order for every launch shape.
+ *   own_sq = (tree * inv) * inv;  total_sq = own_sq + other_sq
+ *   (own_q_lo / own_q_hi are 0; args->other_q must be 0)
+ * Arguments, layouts and errors as in the fp16 calls; contribution rows and
+ * the slot hold bfloat16 bit patterns.  The workspace is the same size. */
+int zero_reduce_check_bf16(const zero_plan_t* plan, int32_t rank, const uint16_t* const* contrib,
+                           const zero_step_args_t* args, float* grad_out, void* workspace,
+                           size_t ws_bytes, zero_step_result_t* dev_result, hipStream_t stream);
+int zero_finalize_bf16(const zero_plan_t* plan, const zero_step_args_t* args,
+                       zero_step_result_t* dev_result, hipStream_t stream);
+int zero_adam_apply_bf16(const zero_plan_t* plan, int32_t rank, const float* grad, float* master,
+                         float* m, float* v, uint16_t* param_bf16_slot,
+                         const zero_step_args_t* args, const zero_step_result_t* dev_result,
+                         hipStream_t stream);
+int zero_reduce_adam_step_bf16(const zero_plan_t* plan, int32_t rank,
+                               const uint16_t* const* contrib, float* master, float* m, float* v,
+                               uint16_t* param_bf16_slot, float* grad_out, void* workspace,
+                               size_t ws_bytes, const zero_step_args_t* args,
+                               zero_step_result_t* dev_result, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* ZeRO-3 / FSDP units: each unit (a run of consecutive tensors, e.g. one
  * transformer block) is flattened and sharded on its own, and one launch of
  * each kernel updates every unit a rank holds.  Pages: "10.6 ZeRO 与 FSDP",

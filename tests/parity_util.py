@@ -120,8 +120,9 @@ def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Opti
         c = orun.shard_contrib(w, p, rank, step, o_scale, begin, count)
         sc = oracle.step_scalars(w.lr, w.betas[0], w.betas[1], w.eps, w.weight_decay, o_t + 1,
                                  w.world_size, o_scale)
-        out = oracle.shard_step(c, op, om, ov, oh, sc, w.max_grad_norm, other_sq=other_sq,
-                                other_overflow=ovf_other)
+        step_fn = oracle.shard_step_bf16 if w.dtype == "bf16" else oracle.shard_step
+        out = step_fn(c, op, om, ov, oh, sc, w.max_grad_norm, other_sq=other_sq,
+                      other_overflow=ovf_other)
         check_result(res, out.fin, step)
         rep = StepReport(step, out.fin.skip, float(out.fin.coef))
         g = dev.fetch("grad")

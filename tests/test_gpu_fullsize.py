@@ -2,10 +2,12 @@
 bench.py times (the whole shard of the rank).
 
 Every step of each workload runs on the GPU.  The oracle checks:
-  * the exact squared-norm integer, overflow flag, norm, clip coefficient and
-    skip decision of the whole shard (computed by the C form of the oracle's
-    reduce statistics from the same host-generated input chunks that are
-    copied to the device);
+  * the exact squared-norm integer (fp16) or the pairwise fp64 tree (bf16),
+    overflow flag, norm, clip coefficient and skip decision of the whole
+    shard (computed by the C form of the oracle's reduce statistics from the
+    same host-generated input chunks that are copied to the device; for bf16
+    each chunk is an aligned power-of-two subtree, and the roots are summed
+    by the oracle's pairwise tree);
   * g, master, m, v and the fp16 slot at ~4k sampled elements (first, last,
     random, and around an injected inf), computed one by one by the numpy
     oracle, bit for bit, with the state carried across steps.
@@ -48,9 +50,12 @@ def _sample_indices(w, rank, shard, k=4096):
 def _feed_and_reduce(dev, step, scale, idx):
     """Generate the step's contributions chunk by chunk on the host, copy each
     chunk to the device, and reduce the same chunk with the C oracle.  Returns
-    (Q, overflow, contributions at idx)."""
+    (Q or, for bf16, the tree value; overflow; contributions at idx)."""
     w, n, count = dev.w, dev.w.world_size, dev.count
     chunk = (1 << 28) // (2 * n)  # 256 MiB of host staging
+    bf16 = w.dtype == "bf16"
+    assert not bf16 or chunk & (chunk - 1) == 0
+    roots = []
     host = torch.empty((n, chunk), dtype=torch.int16, pin_memory=True)
     hnp = host.numpy().view(np.uint16)
     q_total, bad = 0, False
@@ -62,12 +67,18 @@ def _feed_and_reduce(dev, step, scale, idx):
         with torch.cuda.stream(dev.stream):
             for q in range(n):
                 dev.contrib[q, c0:c0 + k].copy_(host[q, :k], non_blocking=True)
-        qc, bc = fast.reduce_stats(hnp, k)
-        q_total += qc
+        if bf16:
+            qc, bc = fast.reduce_tree_bf16(hnp, k, width=chunk)
+            roots.append(qc)
+        else:
+            qc, bc = fast.reduce_stats(hnp, k)
+            q_total += qc
         bad |= bc
         sel = (idx >= c0) & (idx < c0 + k)
         cols[:, sel] = hnp[:, idx[sel] - c0]
         dev.stream.synchronize()
+    if bf16:
+        return oracle.pairwise_sum_f64(np.array(roots)), bad, cols
     return q_total, bad, cols
 
 
@@ -77,6 +88,7 @@ def _cases():
         (synth.FLAT75, 0), (synth.FLAT75, 1),
         (synth.LLAMA3_8B, 0),
         (synth.LLAMA2_70B, 0),
+        (synth.LLAMA3_8B_BF16, 0), (synth.LLAMA3_8B_BF16, 7),
     )]
 
 
@@ -95,7 +107,8 @@ def test_full_size_shard(w, rank):
     flat = rank * p.shard + idx
     op = np.array([synth.masters(w, int(e), 1)[0] for e in flat], dtype=np.float32)
     om, ov = np.zeros_like(op), np.zeros_like(op)
-    oh = op.astype(np.float16).view(np.uint16)
+    bf16 = w.dtype == "bf16"
+    oh = orun.half_copy(w, op)
     other_sq = w.other_sq(p.real(rank)) if w.other_ranks_from_config else 0.0
     scaler = abi.new_scaler(w.loss_scale0)
     o_scale, o_good, o_t = w.loss_scale0, 0, 0
@@ -108,22 +121,23 @@ def test_full_size_shard(w, rank):
         res = dev.result()
         sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, o_t + 1, w.world_size,
                                  o_scale)
-        fin = oracle.finalize(q_all, bad_all, sc.inv64, w.max_grad_norm, other_sq=other_sq,
-                              other_overflow=ovf_other)
+        fin_fn = oracle.finalize_bf16 if bf16 else oracle.finalize
+        fin = fin_fn(q_all, bad_all, sc.inv64, w.max_grad_norm, other_sq=other_sq,
+                     other_overflow=ovf_other)
         check_result(res, fin, step)
-        acc = oracle.reduce_contributions(cols)
+        acc = (oracle.reduce_contributions_bf16 if bf16 else oracle.reduce_contributions)(cols)
         g = oracle.unscale(acc, sc.inv32)
         assert np.array_equal(dev.fetch("grad", idx).view(np.uint32), g.view(np.uint32)), step
         if not fin.skip:
             op, om, ov, h = oracle.adam_apply(g, op, om, ov, sc, fin.coef)
-            oh = h.view(np.uint16)
+            oh = oracle.f32_to_bf16(op) if bf16 else h.view(np.uint16)
         rep = StepReport(step, fin.skip, float(fin.coef))
         for name, want in (("master", op), ("m", om), ("v", ov), ("slot", oh)):
             compare_state(rep, name, dev.fetch(name, idx), want)
         assert all(x == 0 for x in rep.mismatches.values()), (step, rep.mismatches)
         assert dev.guards_intact()
         print(f"  step {step}: skip={fin.skip} coef={float(fin.coef):.6g} norm={fin.norm:.6g} "
-              f"Q bits={q_all.bit_length()}", flush=True)
+              f"stat={q_all if bf16 else q_all.bit_length()}", flush=True)
         skips.append(fin.skip)
         abi.zero_scaler_update(scaler, bool(res.skip))
         o_scale, o_good = oracle.scaler_update(o_scale, o_good, fin.skip)

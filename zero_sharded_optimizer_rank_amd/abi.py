@@ -110,6 +110,16 @@ _SIGNATURES = {
     "zero_reduce_adam_step": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _P(_vp), _vp, _vp,
                                              _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                              _P(zero_step_args_t), _vp, _vp]),
+    "zero_reduce_check_bf16": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _P(_vp),
+                                              _P(zero_step_args_t), _vp, _vp, ctypes.c_size_t,
+                                              _vp, _vp]),
+    "zero_finalize_bf16": (ctypes.c_int, [_P(zero_plan_t), _P(zero_step_args_t), _vp, _vp]),
+    "zero_adam_apply_bf16": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _vp, _vp, _vp, _vp,
+                                            _vp, _P(zero_step_args_t), _vp, _vp]),
+    "zero_reduce_adam_step_bf16": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _P(_vp),
+                                                  _vp, _vp, _vp, _vp, _vp, _vp,
+                                                  ctypes.c_size_t, _P(zero_step_args_t), _vp,
+                                                  _vp]),
     "zero_plan_units": (ctypes.c_int, [_P(ctypes.c_int64), ctypes.c_int32, _P(ctypes.c_int32),
                                        ctypes.c_int32, ctypes.c_int32, _P(zero_unit_plan_t),
                                        _P(zero_unit_info_t), ctypes.c_int32]),
@@ -246,6 +256,34 @@ def zero_reduce_adam_step(plan, rank, contrib, master, m, v, param16_slot, grad_
                                        _addr(master), _addr(m), _addr(v), _addr(param16_slot),
                                        _addr(grad_out), _addr(workspace), ws_bytes,
                                        ctypes.byref(args), _addr(dev_result), _stream(stream)))
+
+
+def zero_reduce_check_bf16(plan, rank, contrib, args, grad_out, workspace, ws_bytes, dev_result,
+                           stream=None):
+    _check(lib().zero_reduce_check_bf16(ctypes.byref(plan), rank, _ptr_array(contrib),
+                                        ctypes.byref(args), _addr(grad_out), _addr(workspace),
+                                        ws_bytes, _addr(dev_result), _stream(stream)))
+
+
+def zero_finalize_bf16(plan, args, dev_result, stream=None):
+    _check(lib().zero_finalize_bf16(ctypes.byref(plan), ctypes.byref(args), _addr(dev_result),
+                                    _stream(stream)))
+
+
+def zero_adam_apply_bf16(plan, rank, grad, master, m, v, param_bf16_slot, args, dev_result,
+                         stream=None):
+    _check(lib().zero_adam_apply_bf16(ctypes.byref(plan), rank, _addr(grad), _addr(master),
+                                      _addr(m), _addr(v), _addr(param_bf16_slot),
+                                      ctypes.byref(args), _addr(dev_result), _stream(stream)))
+
+
+def zero_reduce_adam_step_bf16(plan, rank, contrib, master, m, v, param_bf16_slot, grad_out,
+                               workspace, ws_bytes, args, dev_result, stream=None):
+    _check(lib().zero_reduce_adam_step_bf16(ctypes.byref(plan), rank, _ptr_array(contrib),
+                                            _addr(master), _addr(m), _addr(v),
+                                            _addr(param_bf16_slot), _addr(grad_out),
+                                            _addr(workspace), ws_bytes, ctypes.byref(args),
+                                            _addr(dev_result), _stream(stream)))
 
 
 def zero_plan_units(numels: Sequence[int], unit_of_tensor: Sequence[int], world_size: int,

@@ -78,6 +78,30 @@ __device__ __forceinline__ uint32_t f2h(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
+// bfloat16 <-> fp32: bf16 is the top half of fp32 (widening is exact);
+// narrowing rounds to nearest even, and a NaN stays a quiet NaN.
+__device__ __forceinline__ float bf2f(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+__device__ __forceinline__ uint32_t f2bf(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+enum class Fmt { F16, BF16 };
+
+template <Fmt F>
+__device__ __forceinline__ float to_f32(uint32_t bits) {
+  if constexpr (F == Fmt::BF16) return bf2f(bits);
+  else return h2f(bits);
+}
+
+template <Fmt F>
+__device__ __forceinline__ uint32_t from_f32(float x) {
+  if constexpr (F == Fmt::BF16) return f2bf(x);
+  else return f2h(x);
+}
+
 // acc^2 in units of 2^-48 as a 128-bit integer (lo, hi); sets bad for a
 // non-finite acc, which contributes nothing.  With m the 24-bit significand
 // and e the biased exponent, acc^2 = m^2 * 2^(2e - 300) = m^2 * 2^(2e - 252)
@@ -294,6 +318,7 @@ __device__ __forceinline__ void adam1(float g, float c, const AdamScalars& sc, f
 // lane i writes the word holding its last `me` results and lane i+1's first
 // 4 - me (through a shuffle every lane of the wave takes part in); the pieces
 // at a wave's edges or the segment's end go out as 2-byte stores.
+template <Fmt F = Fmt::F16>
 __device__ inline void adam_quad(const float* __restrict__ grad, float* __restrict__ master,
                                  float* __restrict__ mom, float* __restrict__ var,
                                  uint16_t* __restrict__ slot, int64_t shard, int64_t qd, float c,
@@ -316,7 +341,7 @@ __device__ inline void adam_quad(const float* __restrict__ grad, float* __restri
       p[e] = pp;
       m[e] = mm;
       v[e] = vv;
-      h |= (uint64_t)f2h(pp) << (16 * e);
+      h |= (uint64_t)from_f32<F>(pp) << (16 * e);
     }
     vstore<ZK_K2_NT_STORE>(p, (f32x4*)(master + off));
     vstore<ZK_K2_NT_STORE>(m, (f32x4*)(mom + off));
@@ -347,7 +372,7 @@ __device__ inline void adam_quad(const float* __restrict__ grad, float* __restri
       master[j] = pp;
       mom[j] = mm;
       var[j] = vv;
-      slot[j] = (uint16_t)f2h(pp);
+      slot[j] = (uint16_t)from_f32<F>(pp);
     }
   }
 }
@@ -391,6 +416,202 @@ __device__ inline void reduce_partials_and_finalize(const Partial* __restrict__ 
   if (threadIdx.x == 0) {
     finalize_into(lo, hi, bad, fa, res);
     *ticket = 0u;  // ready for the next call
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// bf16 path: the shard's squared norm is the balanced pairwise tree, in fp64,
+// of the exact squares acc_j^2 over element indices zero-padded to a power of
+// two.  Every level below is a contiguous power-of-two-aligned subtree of that
+// one tree, so the result does not depend on the launch shape.
+
+__device__ __forceinline__ uint64_t shfl_down_bits(uint64_t x, unsigned int d) {
+  return shfl_down_u64(x, d);
+}
+
+__device__ __forceinline__ double sq_or_zero(float acc, uint32_t& bad) {
+  const bool fin = (__float_as_uint(acc) & 0x7F800000u) != 0x7F800000u;
+  bad |= fin ? 0u : 1u;
+  const double a = fin ? (double)acc : 0.0;
+  return a * a;  // exact: at most 48 significant bits, exponent in range
+}
+
+// One quad's tree node: (s0 + s1) + (s2 + s3); elements past the shard are +0.
+template <typename Rows>
+__device__ __forceinline__ double reduce_quad_bf16(const Rows& rows, int32_t n, int64_t qd,
+                                                   int64_t shard, float inv32,
+                                                   float* __restrict__ grad, uint32_t& bad) {
+  const int64_t full = shard >> 2;
+  const int64_t off = qd * 4;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (qd < full) {
+    for (int r0 = 0; r0 < n; r0 += kRankBatch) {
+      u32x2 d[kRankBatch];
+#pragma unroll
+      for (int b = 0; b < kRankBatch; ++b)
+        if (r0 + b < n) d[b] = vload<ZK_K1_NT_LOAD>((const u32x2*)(rows.row(r0 + b) + off));
+#pragma unroll
+      for (int b = 0; b < kRankBatch; ++b) {
+        if (r0 + b < n) {
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            acc[2 * w] = acc[2 * w] + bf2f(d[b][w] & 0xFFFFu);
+            acc[2 * w + 1] = acc[2 * w + 1] + bf2f(d[b][w] >> 16);
+          }
+        }
+      }
+    }
+    f32x4 g;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[e] = acc[e] * inv32;
+    vstore<ZK_K1_NT_STORE>(g, (f32x4*)(grad + off));
+  } else if (qd == full) {
+    for (int64_t j = off; j < shard; ++j) {
+      float a = 0.0f;
+      for (int r = 0; r < n; ++r) a = a + bf2f(rows.row(r)[j]);
+      acc[j - off] = a;
+      grad[j] = a * inv32;
+    }
+  } else {
+    return 0.0;
+  }
+  return (sq_or_zero(acc[0], bad) + sq_or_zero(acc[1], bad)) +
+         (sq_or_zero(acc[2], bad) + sq_or_zero(acc[3], bad));
+}
+
+// Tree over the T quad nodes of a workgroup (wave shuffles, then LDS across
+// waves); the subtree and the OR of the flags land in thread 0.
+template <int T>
+__device__ inline void block_tree(double& x, uint32_t& bad) {
+  static_assert(T % 64 == 0 && (T & (T - 1)) == 0, "a power-of-two number of whole waves");
+  const uint32_t lane = threadIdx.x & 63u;
+  for (unsigned int d = 1; d < 64; d <<= 1) {
+    const double y = __longlong_as_double((long long)shfl_down_bits(
+        (uint64_t)__double_as_longlong(x), d));
+    if ((lane & (2 * d - 1)) == 0) x = x + y;  // left child + right child
+    bad |= (uint32_t)__shfl_xor((int)bad, (int)d);
+  }
+  if constexpr (T == 64) return;
+  __shared__ double s_x[T / 64];
+  __shared__ uint32_t s_bad[T / 64];
+  const int wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    s_x[wave] = x;
+    s_bad[wave] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < T / 64; w <<= 1)
+      for (int i = 0; i < T / 64; i += 2 * w) s_x[i] = s_x[i] + s_x[i + w];
+    x = s_x[0];
+    for (int w = 1; w < T / 64; ++w) bad |= s_bad[w];
+  }
+}
+
+// Reduce kernel body (bf16): workgroup covers quads [q_first, q_first + T),
+// one quad per thread; returns the subtree partial (value bits in lo, flag in
+// bit 63 of hi) in thread 0.
+template <typename Rows>
+__device__ inline Partial reduce_block_bf16(const Rows& rows, int32_t n, int64_t shard,
+                                            int64_t q_first, float inv32,
+                                            float* __restrict__ grad) {
+  uint32_t bad = 0;
+  double x = reduce_quad_bf16(rows, n, q_first + threadIdx.x, shard, inv32, grad, bad);
+  block_tree<ZK_K1_THREADS>(x, bad);
+  return Partial{(uint64_t)__double_as_longlong(x), (uint64_t)(bad ? 1u : 0u) << 63};
+}
+
+__device__ inline void finalize_bf16_into(double tree, uint32_t bad, const FinalizeArgs& fa,
+                                          zero_step_result_t* res) {
+  const double own = (tree * fa.inv64) * fa.inv64;
+  const double tot = own + fa.other_sq;
+  const double norm = __builtin_sqrt(tot);
+  double coef = 1.0;
+  if (fa.max_norm > 0.0) {
+    const double c = fa.max_norm / (norm + 1e-6);
+    coef = (c < 1.0) ? c : 1.0;
+  }
+  res->own_q_lo = 0;
+  res->own_q_hi = 0;
+  res->own_sq = own;
+  res->total_sq = tot;
+  res->norm = norm;
+  res->clip_coef = (float)coef;
+  res->overflow = bad ? 1 : 0;
+  res->skip = (bad || fa.other_overflow) ? 1 : 0;
+  res->reserved = 0;
+}
+
+constexpr int kTreeChunk = 4096;  // most partials one workgroup of the tree kernel sums
+
+// LDS tree over `count` values (count a power of two, <= kTreeChunk) held in
+// s[0..count); the result lands in s[0].
+__device__ inline void lds_tree(double* s, int count) {
+  for (int w = 1; w < count; w <<= 1) {
+    __syncthreads();
+    for (int i = (int)threadIdx.x * 2 * w; i < count; i += kThreads * 2 * w) s[i] = s[i] + s[i + w];
+  }
+  __syncthreads();
+}
+
+// Tree kernel body (bf16): workgroup j sums partials [j*chunk, (j+1)*chunk)
+// (chunk a power of two; partials past n_partials count +0) into a level-2
+// node; the last workgroup (ticket) sums the level-2 nodes, zero-padded to a
+// power of two, and finalizes.
+__device__ inline void tree_partials_and_finalize_bf16(const Partial* __restrict__ partials,
+                                                       int64_t n_partials, int chunk,
+                                                       Partial* __restrict__ level2,
+                                                       uint32_t* __restrict__ ticket,
+                                                       const FinalizeArgs& fa,
+                                                       zero_step_result_t* __restrict__ res) {
+  __shared__ double s[kTreeChunk];
+  __shared__ uint32_t s_bad;
+  __shared__ uint32_t s_last;
+  if (threadIdx.x == 0) s_bad = 0u;
+  __syncthreads();
+  uint32_t bad = 0;
+  const int64_t base = (int64_t)blockIdx.x * chunk;
+  for (int i = threadIdx.x; i < chunk; i += kThreads) {
+    double v = 0.0;
+    if (base + i < n_partials) {
+      const Partial pt = partials[base + i];
+      v = __longlong_as_double((long long)pt.lo);
+      bad |= (uint32_t)(pt.hi >> 63);
+    }
+    s[i] = v;
+  }
+  if (bad) atomicOr(&s_bad, 1u);
+  lds_tree(s, chunk);
+  if (threadIdx.x == 0) {
+    level2[blockIdx.x] = Partial{(uint64_t)__double_as_longlong(s[0]),
+                                 (uint64_t)(s_bad ? 1u : 0u) << 63};
+    __threadfence();
+    const uint32_t prev = atomicAdd(ticket, 1u);
+    s_last = (prev == gridDim.x - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  int count = 1;
+  while (count < (int)gridDim.x) count <<= 1;
+  bad = 0;
+  for (int i = threadIdx.x; i < count; i += kThreads) {
+    double v = 0.0;
+    if (i < (int)gridDim.x) {
+      const Partial pt = level2[i];
+      v = __longlong_as_double((long long)pt.lo);
+      bad |= (uint32_t)(pt.hi >> 63);
+    }
+    s[i] = v;
+  }
+  if (threadIdx.x == 0) s_bad = 0u;
+  __syncthreads();
+  if (bad) atomicOr(&s_bad, 1u);
+  lds_tree(s, count);
+  if (threadIdx.x == 0) {
+    finalize_bf16_into(s[0], s_bad, fa, res);
+    *ticket = 0u;
   }
 }
 

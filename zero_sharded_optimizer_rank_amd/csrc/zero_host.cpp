@@ -276,6 +276,70 @@ int zero_reduce_adam_step(const zero_plan_t* plan, int32_t rank, const uint16_t*
                          stream);
 }
 
+int zero_reduce_check_bf16(const zero_plan_t* plan, int32_t rank, const uint16_t* const* contrib,
+                           const zero_step_args_t* args, float* grad_out, void* workspace,
+                           size_t ws_bytes, zero_step_result_t* dev_result, hipStream_t stream) {
+  g_err[0] = 0;
+  int rc = check_plan_rank(plan, rank);
+  if (!rc) rc = check_norm_args(args);
+  if (!rc && (args->other_q_lo || args->other_q_hi))
+    rc = fail(ZERO_EINVAL, "the bf16 path takes the other ranks' share as other_sq only");
+  if (!rc) rc = check_reduce_ptrs(plan, contrib, grad_out, workspace, ws_bytes, dev_result);
+  if (rc) return rc;
+  const zk::FinalizeArgs fa = finalize_args(plan, args);
+  return hip_status(zk::launch_reduce_check_bf16(contrib, (int)plan->world_size, plan->shard,
+                                                 (float)fa.inv64, grad_out, workspace, fa,
+                                                 dev_result, stream),
+                    "bf16 reduce_check launch");
+}
+
+int zero_finalize_bf16(const zero_plan_t* plan, const zero_step_args_t* args,
+                       zero_step_result_t* dev_result, hipStream_t stream) {
+  g_err[0] = 0;
+  int rc = check_plan_rank(plan, 0);
+  if (!rc) rc = check_norm_args(args);
+  if (!rc && (args->other_q_lo || args->other_q_hi))
+    rc = fail(ZERO_EINVAL, "the bf16 path takes the other ranks' share as other_sq only");
+  if (rc) return rc;
+  if (!dev_result) return fail(ZERO_EINVAL, "dev_result is NULL");
+  if (!aligned(dev_result, 8)) return fail(ZERO_EALIGN, "dev_result not 8-byte aligned");
+  return hip_status(zk::launch_finalize_bf16(finalize_args(plan, args), dev_result, stream),
+                    "bf16 finalize launch");
+}
+
+int zero_adam_apply_bf16(const zero_plan_t* plan, int32_t rank, const float* grad, float* master,
+                         float* m, float* v, uint16_t* param_bf16_slot,
+                         const zero_step_args_t* args, const zero_step_result_t* dev_result,
+                         hipStream_t stream) {
+  g_err[0] = 0;
+  int rc = check_plan_rank(plan, rank);
+  if (!rc) rc = check_adam_args(args);
+  if (!rc) rc = check_adam_ptrs(plan, grad, master, m, v, param_bf16_slot, dev_result);
+  if (rc) return rc;
+  if (plan->shard == 0) return ZERO_OK;
+  return hip_status(zk::launch_adam_bf16(grad, master, m, v, param_bf16_slot, plan->shard,
+                                         adam_scalars(args), dev_result, stream),
+                    "bf16 adam launch");
+}
+
+int zero_reduce_adam_step_bf16(const zero_plan_t* plan, int32_t rank,
+                               const uint16_t* const* contrib, float* master, float* m, float* v,
+                               uint16_t* param_bf16_slot, float* grad_out, void* workspace,
+                               size_t ws_bytes, const zero_step_args_t* args,
+                               zero_step_result_t* dev_result, hipStream_t stream) {
+  g_err[0] = 0;
+  int rc = check_plan_rank(plan, rank);
+  if (!rc) rc = check_adam_args(args);
+  if (!rc) rc = check_reduce_ptrs(plan, contrib, grad_out, workspace, ws_bytes, dev_result);
+  if (!rc) rc = check_adam_ptrs(plan, grad_out, master, m, v, param_bf16_slot, dev_result);
+  if (rc) return rc;
+  rc = zero_reduce_check_bf16(plan, rank, contrib, args, grad_out, workspace, ws_bytes, dev_result,
+                              stream);
+  if (rc) return rc;
+  return zero_adam_apply_bf16(plan, rank, grad_out, master, m, v, param_bf16_slot, args,
+                              dev_result, stream);
+}
+
 int zero_plan_units(const int64_t* numels, int32_t n_tensors, const int32_t* unit_of_tensor,
                     int32_t world_size, int32_t align_elems, zero_unit_plan_t* plan_out,
                     zero_unit_info_t* units_out, int32_t units_cap) {

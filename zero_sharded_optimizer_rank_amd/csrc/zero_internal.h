@@ -50,6 +50,16 @@ int launch_adam(const float* grad, float* master, float* m, float* v, uint16_t* 
                 hipStream_t stream);
 void* workspace_partials(void* workspace);
 
+// bf16 path (the norm is a fixed pairwise fp64 tree; see zero_device.h).
+int64_t k1_blocks_bf16(int64_t shard);
+int launch_reduce_check_bf16(const uint16_t* const* contrib, int n, int64_t shard, float inv32,
+                             float* grad, void* workspace, const FinalizeArgs& fa,
+                             zero_step_result_t* res, hipStream_t stream);
+int launch_finalize_bf16(const FinalizeArgs& fa, zero_step_result_t* res, hipStream_t stream);
+int launch_adam_bf16(const float* grad, float* master, float* m, float* v, uint16_t* slot,
+                     int64_t shard, const AdamScalars& sc, const zero_step_result_t* res,
+                     hipStream_t stream);
+
 // Multi-unit forms (zero_units.hip): the unit table lives in device memory.
 int launch_units_reduce(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
                         int n, float inv32, void* workspace, hipStream_t stream);

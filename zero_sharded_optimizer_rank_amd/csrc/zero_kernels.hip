@@ -69,7 +69,62 @@ __global__ __launch_bounds__(ZK_K2_THREADS) void k2_adam(
   }
 }
 
+// --- bf16 path -------------------------------------------------------------
+__global__ __launch_bounds__(ZK_K1_THREADS) void k1_reduce_check_bf16(
+    ContribTable ct, int32_t n, int64_t shard, float inv32, float* __restrict__ grad,
+    Partial* __restrict__ partials, uint32_t* __restrict__ ticket) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;  // arm the tree kernel's ticket
+  const int64_t q_first = (int64_t)blockIdx.x * ZK_K1_THREADS;
+  const Partial pt = reduce_block_bf16(ct, n, shard, q_first, inv32, grad);
+  if (threadIdx.x == 0) partials[blockIdx.x] = pt;
+}
+
+__global__ __launch_bounds__(kThreads) void kt_tree_finalize_bf16(
+    const Partial* __restrict__ partials, int64_t n_partials, int chunk,
+    Partial* __restrict__ level2, uint32_t* __restrict__ ticket, FinalizeArgs fa,
+    zero_step_result_t* __restrict__ res) {
+  tree_partials_and_finalize_bf16(partials, n_partials, chunk, level2, ticket, fa, res);
+}
+
+__global__ void k_finalize_bf16(FinalizeArgs fa, zero_step_result_t* res) {
+  // re-finalize from the stored own share (own_sq) with new other-rank values
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    const double own = res->own_sq;
+    const uint32_t bad = (uint32_t)res->overflow;
+    const double tot = own + fa.other_sq;
+    const double norm = __builtin_sqrt(tot);
+    double coef = 1.0;
+    if (fa.max_norm > 0.0) {
+      const double c = fa.max_norm / (norm + 1e-6);
+      coef = (c < 1.0) ? c : 1.0;
+    }
+    res->total_sq = tot;
+    res->norm = norm;
+    res->clip_coef = (float)coef;
+    res->skip = (bad || fa.other_overflow) ? 1 : 0;
+  }
+}
+
+__global__ __launch_bounds__(ZK_K2_THREADS) void k2_adam_bf16(
+    const float* __restrict__ grad, float* __restrict__ master, float* __restrict__ mom,
+    float* __restrict__ var, uint16_t* __restrict__ slot, int64_t shard, AdamScalars sc,
+    const zero_step_result_t* __restrict__ res) {
+  if (res->skip) return;
+  const float c = res->clip_coef;
+#pragma unroll
+  for (int u = 0; u < ZK_K2_QUADS; ++u) {
+    const int64_t qd = ((int64_t)blockIdx.x * ZK_K2_QUADS + u) * ZK_K2_THREADS + threadIdx.x;
+    adam_quad<Fmt::BF16>(grad, master, mom, var, slot, shard, qd, c, sc);
+  }
+}
+
 }  // namespace
+
+int64_t k1_blocks_bf16(int64_t shard) {
+  const int64_t quads = (shard + 3) >> 2;
+  const int64_t b = (quads + ZK_K1_THREADS - 1) / ZK_K1_THREADS;
+  return b < 1 ? 1 : b;
+}
 
 int64_t k1_blocks(int64_t shard) {
   const int64_t units = (shard + 3) >> 2;  // quads, the ragged one included
@@ -89,7 +144,10 @@ size_t workspace_bytes_for_blocks(int64_t reduce_blocks) {
   return kTicketBytes + (size_t)kFinBlocks * kPartialBytes + (size_t)reduce_blocks * kPartialBytes;
 }
 
-size_t workspace_bytes(int64_t shard) { return workspace_bytes_for_blocks(k1_blocks(shard)); }
+size_t workspace_bytes(int64_t shard) {
+  const int64_t a = k1_blocks(shard), b = k1_blocks_bf16(shard);
+  return workspace_bytes_for_blocks(a > b ? a : b);
+}
 
 void* workspace_partials(void* workspace) {
   return (char*)workspace + kTicketBytes + (size_t)kFinBlocks * kPartialBytes;
@@ -133,6 +191,43 @@ int launch_finalize_empty(const FinalizeArgs& fa, zero_step_result_t* res, hipSt
 
 int launch_finalize(const FinalizeArgs& fa, zero_step_result_t* res, hipStream_t stream) {
   hipLaunchKernelGGL(k_finalize, dim3(1), dim3(64), 0, stream, fa, res);
+  return (int)hipGetLastError();
+}
+
+int launch_reduce_check_bf16(const uint16_t* const* contrib, int n, int64_t shard, float inv32,
+                             float* grad, void* workspace, const FinalizeArgs& fa,
+                             zero_step_result_t* res, hipStream_t stream) {
+  ContribTable ct;
+  for (int r = 0; r < ZERO_MAX_RANKS; ++r) ct.p[r] = r < n ? contrib[r] : nullptr;
+  const int64_t blocks = k1_blocks_bf16(shard);
+  uint32_t* ticket = (uint32_t*)workspace;
+  Partial* level2 = (Partial*)((char*)workspace + kTicketBytes);
+  Partial* partials = (Partial*)workspace_partials(workspace);
+  hipLaunchKernelGGL(k1_reduce_check_bf16, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), 0, stream,
+                     ct, n, shard, inv32, grad, partials, ticket);
+  int e = (int)hipGetLastError();
+  if (e != hipSuccess) return e;
+  // chunk: a power of two with at most kFinBlocks workgroups over all partials
+  int64_t per = (blocks + kFinBlocks - 1) / kFinBlocks;
+  int64_t chunk = 1;
+  while (chunk < per) chunk <<= 1;
+  if (chunk > kTreeChunk) return (int)hipErrorInvalidValue;
+  const int64_t fb = (blocks + chunk - 1) / chunk;
+  hipLaunchKernelGGL(kt_tree_finalize_bf16, dim3((uint32_t)fb), dim3(kThreads), 0, stream,
+                     partials, blocks, (int)chunk, level2, ticket, fa, res);
+  return (int)hipGetLastError();
+}
+
+int launch_finalize_bf16(const FinalizeArgs& fa, zero_step_result_t* res, hipStream_t stream) {
+  hipLaunchKernelGGL(k_finalize_bf16, dim3(1), dim3(64), 0, stream, fa, res);
+  return (int)hipGetLastError();
+}
+
+int launch_adam_bf16(const float* grad, float* master, float* m, float* v, uint16_t* slot,
+                     int64_t shard, const AdamScalars& sc, const zero_step_result_t* res,
+                     hipStream_t stream) {
+  hipLaunchKernelGGL(k2_adam_bf16, dim3((uint32_t)k2_blocks(shard)), dim3(ZK_K2_THREADS), 0,
+                     stream, grad, master, m, v, slot, shard, sc, res);
   return (int)hipGetLastError();
 }
 

@@ -47,6 +47,9 @@ class DeviceShard:
         if not (0 <= begin and begin + count <= s_full):
             raise ValueError("window outside the shard")
         self.begin, self.count = begin, count
+        if w.dtype not in ("fp16", "bf16"):
+            raise ValueError(f"unknown gradient format {w.dtype!r}")
+        self.bf16 = w.dtype == "bf16"
         self.flat_begin = rank * s_full + begin  # flat index of the window's first element
         real = max(0, min(count, w.psi - self.flat_begin))
         n = w.world_size
@@ -112,7 +115,8 @@ class DeviceShard:
             self._feed16(self.contrib[q], fill)
 
     def load_initial_state(self):
-        """Seeded fp32 masters, m = v = 0, and the slot = fp16(master)."""
+        """Seeded fp32 masters, m = v = 0, and the slot = fp16 (or bf16) of the
+        master, rounded to nearest even."""
         with torch.cuda.stream(self.stream):
             for s in range(0, self.count, self._chunk):
                 k = min(self._chunk, self.count - s)
@@ -121,7 +125,8 @@ class DeviceShard:
                 self.stream.synchronize()
             self.m.zero_()
             self.v.zero_()
-            self.slot.copy_(self.master[:self.count].to(torch.float16).view(torch.int16))
+            half = torch.bfloat16 if self.bf16 else torch.float16
+            self.slot.copy_(self.master[:self.count].to(half).view(torch.int16))
         self.stream.synchronize()
 
     # ------------------------------------------------------------------ steps
@@ -135,18 +140,22 @@ class DeviceShard:
                              other_q=other_q, other_overflow=other_overflow)
 
     def reduce_check(self, args):
-        abi.zero_reduce_check(self.plan, self.rank_in_plan, self.contrib_ptrs(), args, self.grad,
+        f = abi.zero_reduce_check_bf16 if self.bf16 else abi.zero_reduce_check
+        f(self.plan, self.rank_in_plan, self.contrib_ptrs(), args, self.grad,
                               self.ws, self.ws.numel(), self.res, self.stream)
 
     def finalize(self, args):
-        abi.zero_finalize(self.plan, args, self.res, self.stream)
+        f = abi.zero_finalize_bf16 if self.bf16 else abi.zero_finalize
+        f(self.plan, args, self.res, self.stream)
 
     def adam_apply(self, args):
-        abi.zero_adam_apply(self.plan, self.rank_in_plan, self.grad, self.master, self.m, self.v,
+        f = abi.zero_adam_apply_bf16 if self.bf16 else abi.zero_adam_apply
+        f(self.plan, self.rank_in_plan, self.grad, self.master, self.m, self.v,
                             self.slot_ptr(), args, self.res, self.stream)
 
     def step(self, args):
-        abi.zero_reduce_adam_step(self.plan, self.rank_in_plan, self.contrib_ptrs(), self.master,
+        f = abi.zero_reduce_adam_step_bf16 if self.bf16 else abi.zero_reduce_adam_step
+        f(self.plan, self.rank_in_plan, self.contrib_ptrs(), self.master,
                                   self.m, self.v, self.slot_ptr(), self.grad, self.ws,
                                   self.ws.numel(), args, self.res, self.stream)
 

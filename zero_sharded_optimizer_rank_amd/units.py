@@ -28,6 +28,8 @@ class DeviceUnits:
     def __init__(self, w: synth.Workload, rank: int, device: str = "cuda:0",
                  stream: Optional[torch.cuda.Stream] = None):
         assert w.units is not None
+        if w.dtype != "fp16":
+            raise ValueError("the unit path takes fp16 contributions and slots")
         self.w, self.rank = w, rank
         self.device = torch.device(device)
         self.stream = stream or torch.cuda.current_stream(self.device)
