@@ -136,6 +136,7 @@ def main():
                    else ("k1_reduce_check", "k2_adam"))
     stream = dev.stream
     n = w.world_size
+    n_units = getattr(dev, "n_units", None)
     other_sq = w.other_sq(real) if w.other_ranks_from_config else 0.0
     t_setup = time.perf_counter()
     dev.load_initial_state()
@@ -223,7 +224,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: rank {a.rank} of N={n}, shard S={S} "
                                f"(psi={w.psi}), {w.dtype} contributions and slot, fp32 master/m/v"
-                               + (f", {dev.n_units} FSDP units" if w.units else ""),
+                               + (f", {n_units} FSDP units" if w.units else ""),
                    "world_size_simulated": n, "shard": S, "psi": w.psi},
         "hbm_gbps_step": (2 * n + 34) * S / (ms_per_step * 1e6),
         "hbm_gbps_step_floor_bytes": (2 * n + 26) * S / (ms_per_step * 1e6),
