@@ -106,6 +106,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--row-align", type=int, default=None,
                     help="contribution row stride alignment in elements (default: the runtime's)")
+    ap.add_argument("--offload", action="store_true",
+                    help="time the offload form: reduce on the GPU, Adam on the host from "
+                         "host-resident state, fp16 parameters back over PCIe")
+    ap.add_argument("--threads", type=int, default=0,
+                    help="host threads of the offload form (0: the CPUs this process may use)")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="offload form: both PCIe directions on one stream")
     ap.add_argument("--calib-bytes", type=float, default=4e9,
                     help="bytes of the calibration copy timed next to the step (0: skip)")
     a = ap.parse_args()
@@ -122,6 +129,8 @@ def main():
 
     abi.lib()
     w = synth.BY_NAME[a.workload]
+    if a.offload:
+        return offload_main(a, w)
     if w.units is not None:
         from zero_sharded_optimizer_rank_amd.units import DeviceUnits
         dev = DeviceUnits(w, a.rank)
@@ -236,6 +245,65 @@ def main():
     }
     if not a.no_cpu_baseline and w.units is None:
         out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def offload_main(a, w):
+    """One JSON line for the offload form of the step (not the default line)."""
+    import torch
+    from zero_sharded_optimizer_rank_amd import abi
+    from zero_sharded_optimizer_rank_amd.shard import OffloadShard
+
+    dev = OffloadShard(w, a.rank, chunk=1 << 22, threads=a.threads or None,
+                       two_streams=not a.one_stream)
+    real = abi.zero_plan_real(dev.full_plan, a.rank)
+    S, n = dev.count, w.world_size
+    other_sq = w.other_sq(real) if w.other_ranks_from_config else 0.0
+    dev.load_initial_state()
+    dev.load_contributions(1, w.loss_scale0)
+    stream = dev.stream
+    for i in range(a.warmup):
+        dev.reduce_check(dev.args(i + 1, w.loss_scale0, other_sq=other_sq))
+        dev.adam_apply(dev.args(i + 1, w.loss_scale0, other_sq=other_sq))
+    k1_ms, host_s = [], []
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        args = dev.args(a.warmup + i + 1, w.loss_scale0, other_sq=other_sq)
+        ev[0].record(stream)
+        dev.reduce_check(args)
+        ev[1].record(stream)
+        t1 = time.perf_counter()
+        res = dev.adam_apply(args)  # waits for the reduce, then runs the pipeline
+        host_s.append(time.perf_counter() - t1)
+        k1_ms.append(ev[0].elapsed_time(ev[1]))
+        if res.skip:
+            raise RuntimeError("a timed step was skipped")
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / a.steps
+    k1 = sum(k1_ms) / a.steps
+    pipe = sum(host_s) / a.steps - k1 / 1e3
+    b1, _ = bytes_per_param(n)
+    out = {
+        "metric": "params updated/sec, offload form of the shard step (host Adam, PCIe)",
+        "value": real / (ms / 1e3), "unit": "params/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name}: rank {a.rank} of N={n}, shard S={S}, fp16 contributions "
+                               f"and slot on the GPU, fp32 master/m/v in host memory, "
+                               f"{dev.threads} host threads, 4M-element PCIe chunks, "
+                               + ("one stream" if a.one_stream else "upload on a second stream"),
+                   "world_size_simulated": n, "shard": S, "psi": w.psi},
+        "roofline": {"bound": "pcie", "kernel": "offload pipeline",
+                     "achieved": 6 * S / (pipe * 1e9), "peak": 64.0, "unit": "GB/s",
+                     "frac": 6 * S / (pipe * 1e9) / 64.0, "traffic": None},
+        "offload": {"k1_ms": k1, "pipeline_ms": pipe * 1e3,
+                    "pcie_gbps": 6 * S / (pipe * 1e9),
+                    "host_state_gbps": 30 * S / (pipe * 1e9),
+                    "k1_gbps": b1 * S / (k1 * 1e6)},
+        "kernel_hash": kernel_hash(),
+    }
     print(json.dumps(out), flush=True)
 
 

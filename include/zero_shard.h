@@ -263,6 +263,80 @@ int zero_reduce_adam_step_bf16(const zero_plan_t* plan, int32_t rank,
                                zero_step_result_t* dev_result, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* ZeRO-Offload form of the update ("10.6 ZeRO 与 FSDP" §10.6.6: the GPU
+ * keeps forward and backward, gradients travel to the CPU over PCIe, the CPU
+ * updates the parameters from optimizer state held in host memory and sends
+ * the fp16 parameters back; the tutorial's offload_optimizer setting).  The
+ * reduce, unscale, overflow check and norm stay on the GPU (zero_reduce_check);
+ * the fp32 master, m and v live in host memory; the host runs the same
+ * separately rounded fp32 Adam sequence as the GPU kernel, so the results
+ * are identical bit for bit. */
+
+#define ZERO_MAX_HOST_THREADS 256
+
+/* Pinned host staging for the PCIe pipeline, caller-owned (allocate it with
+ * hipHostMalloc or an equivalent pinned allocation): two chunks of fp32
+ * gradient and two of fp16 parameters, used alternately so that copies in
+ * both directions overlap the host's arithmetic. */
+typedef struct zero_offload_staging {
+  float* grad_pinned;       /* [2 * chunk] */
+  uint16_t* param16_pinned; /* [2 * chunk] */
+  int64_t chunk;            /* elements per pipeline chunk: a positive multiple of 64 */
+  hipStream_t upload_stream; /* stream for the host-to-device copies of the fp16 chunks, so
+                                both PCIe directions run at once; NULL: the call's stream.
+                                Caller-owned, default priority. */
+} zero_offload_staging_t;
+
+/* Bytes of pinned staging for a chunk size (both buffers); 0 if chunk is not
+ * a positive multiple of 64. */
+size_t zero_offload_staging_bytes(int64_t chunk);
+
+/*
+ * zero_host_adam_apply: the host update on host arrays of `count` elements:
+ * Adam/AdamW with clip coefficient clip_coef (in (0, 1]) on grad, in place on
+ * master, m, v, and the fp16 (round to nearest even) copy of the new master
+ * into param16.  No alignment needed.  threads: 1..ZERO_MAX_HOST_THREADS
+ * worker threads (the caller's included).  vector_width: 0 = the widest
+ * available, 1 = scalar, 8 = AVX2 + F16C, 16 = AVX-512F; every width gives
+ * the same bits.  Synchronous; no GPU involved.
+ * Errors: ZERO_EINVAL (bad args as zero_adam_apply, count < 0, NULL arrays,
+ * clip_coef outside (0, 1], threads out of range, a width the CPU lacks).
+ */
+int zero_host_adam_apply(const float* grad, float* master, float* m, float* v,
+                         uint16_t* param16, int64_t count, const zero_step_args_t* args,
+                         float clip_coef, int32_t threads, int32_t vector_width);
+
+/*
+ * zero_offload_adam_apply: the update of the offload form.  Reads the step
+ * result (dev_result, written by zero_reduce_check on `stream`), waits for
+ * it, and copies it to *result_out when result_out is not NULL.  On a skip it
+ * returns with nothing changed.  Otherwise it streams grad_dev (device,
+ * fp32 [S]) to the host chunk by chunk, updates master_host, m_host, v_host
+ * (host fp32 [S], in place, any alignment) and copies the fp16 parameters
+ * into param16_slot_dev (device, = flat16 + rank*S, 2-byte aligned).  The
+ * gradient copies run on `stream`, the parameter copies on the staging's
+ * upload stream (or `stream`); the call returns when the last copy has
+ * finished.
+ * Errors: as zero_adam_apply, plus ZERO_EINVAL for bad staging or threads.
+ * After a ZERO_EHIP in the middle, the host state may be partly updated.
+ */
+int zero_offload_adam_apply(const zero_plan_t* plan, int32_t rank, const float* grad_dev,
+                            float* master_host, float* m_host, float* v_host,
+                            uint16_t* param16_slot_dev, const zero_step_args_t* args,
+                            const zero_step_result_t* dev_result,
+                            const zero_offload_staging_t* staging, int32_t threads,
+                            zero_step_result_t* result_out, hipStream_t stream);
+
+/* zero_offload_step: zero_reduce_check on the GPU, then
+ * zero_offload_adam_apply; arguments as those two calls. */
+int zero_offload_step(const zero_plan_t* plan, int32_t rank, const uint16_t* const* contrib,
+                      float* grad_dev, void* workspace, size_t ws_bytes, float* master_host,
+                      float* m_host, float* v_host, uint16_t* param16_slot_dev,
+                      const zero_step_args_t* args, zero_step_result_t* dev_result,
+                      const zero_offload_staging_t* staging, int32_t threads,
+                      zero_step_result_t* result_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* ZeRO-3 / FSDP units: each unit (a run of consecutive tensors, e.g. one
  * transformer block) is flattened and sharded on its own, and one launch of
  * each kernel updates every unit a rank holds.  Pages: "10.6 ZeRO 与 FSDP",

@@ -84,14 +84,19 @@ def other_overflow_at(w: synth.Workload, step: int, flat_begin: int, count: int)
 
 def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Optional[int] = None,
                fused: bool = True, strict: bool = True,
-               ws_fill: Optional[int] = None) -> List[StepReport]:
+               ws_fill: Optional[int] = None, offload: Optional[dict] = None) -> List[StepReport]:
     """Run `steps` steps of the workload on one window of rank's shard on the
-    GPU and in the oracle; compare every step."""
+    GPU and in the oracle; compare every step.  With `offload` (OffloadShard
+    keyword arguments) the update runs in the offload form: host state, PCIe
+    pipeline."""
     import zero_sharded_optimizer_rank_amd.abi as abi
-    from zero_sharded_optimizer_rank_amd.shard import DeviceShard
+    from zero_sharded_optimizer_rank_amd.shard import DeviceShard, OffloadShard
 
     steps = w.steps if steps is None else steps
-    dev = DeviceShard(w, rank, begin, count)
+    if offload is not None:
+        dev = OffloadShard(w, rank, begin, count, **offload)
+    else:
+        dev = DeviceShard(w, rank, begin, count)
     dev.load_initial_state()
     p = orun.workload_plan(w)
     flat_begin = rank * p.shard + begin

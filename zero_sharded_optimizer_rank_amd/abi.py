@@ -85,6 +85,11 @@ class zero_unit_buffers_t(ctypes.Structure):
                 ("reduce_block", ctypes.c_int64), ("adam_block", ctypes.c_int64)]
 
 
+class zero_offload_staging_t(ctypes.Structure):
+    _fields_ = [("grad_pinned", ctypes.c_void_p), ("param16_pinned", ctypes.c_void_p),
+                ("chunk", ctypes.c_int64), ("upload_stream", ctypes.c_void_p)]
+
+
 RESULT_BYTES = ctypes.sizeof(zero_step_result_t)
 UNIT_BUFFERS_BYTES = ctypes.sizeof(zero_unit_buffers_t)
 
@@ -120,6 +125,18 @@ _SIGNATURES = {
                                                   _vp, _vp, _vp, _vp, _vp, _vp,
                                                   ctypes.c_size_t, _P(zero_step_args_t), _vp,
                                                   _vp]),
+    "zero_offload_staging_bytes": (ctypes.c_size_t, [ctypes.c_int64]),
+    "zero_host_adam_apply": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
+                                            _P(zero_step_args_t), ctypes.c_float, ctypes.c_int32,
+                                            ctypes.c_int32]),
+    "zero_offload_adam_apply": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _vp, _vp, _vp,
+                                               _vp, _vp, _P(zero_step_args_t), _vp,
+                                               _P(zero_offload_staging_t), ctypes.c_int32,
+                                               _P(zero_step_result_t), _vp]),
+    "zero_offload_step": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _P(_vp), _vp, _vp,
+                                         ctypes.c_size_t, _vp, _vp, _vp, _vp,
+                                         _P(zero_step_args_t), _vp, _P(zero_offload_staging_t),
+                                         ctypes.c_int32, _P(zero_step_result_t), _vp]),
     "zero_plan_units": (ctypes.c_int, [_P(ctypes.c_int64), ctypes.c_int32, _P(ctypes.c_int32),
                                        ctypes.c_int32, ctypes.c_int32, _P(zero_unit_plan_t),
                                        _P(zero_unit_info_t), ctypes.c_int32]),
@@ -160,6 +177,8 @@ def _addr(x) -> int:
         return 0
     if isinstance(x, int):
         return x
+    if hasattr(x, "__array_interface__"):  # numpy array in host memory
+        return int(x.__array_interface__["data"][0])
     return int(x.data_ptr())
 
 
@@ -284,6 +303,45 @@ def zero_reduce_adam_step_bf16(plan, rank, contrib, master, m, v, param_bf16_slo
                                             _addr(param_bf16_slot), _addr(grad_out),
                                             _addr(workspace), ws_bytes, ctypes.byref(args),
                                             _addr(dev_result), _stream(stream)))
+
+
+def zero_offload_staging_bytes(chunk):
+    return int(lib().zero_offload_staging_bytes(chunk))
+
+
+def offload_staging(grad_pinned, param16_pinned, chunk, upload_stream=None):
+    return zero_offload_staging_t(_addr(grad_pinned), _addr(param16_pinned), chunk,
+                                  _stream(upload_stream))
+
+
+def zero_host_adam_apply(grad, master, m, v, param16, count, args, clip_coef, threads=1,
+                         vector_width=0):
+    _check(lib().zero_host_adam_apply(_addr(grad), _addr(master), _addr(m), _addr(v),
+                                      _addr(param16), count, ctypes.byref(args), clip_coef,
+                                      threads, vector_width))
+
+
+def zero_offload_adam_apply(plan, rank, grad_dev, master_host, m_host, v_host, param16_slot_dev,
+                            args, dev_result, staging, threads=1, stream=None):
+    out = zero_step_result_t()
+    _check(lib().zero_offload_adam_apply(ctypes.byref(plan), rank, _addr(grad_dev),
+                                         _addr(master_host), _addr(m_host), _addr(v_host),
+                                         _addr(param16_slot_dev), ctypes.byref(args),
+                                         _addr(dev_result), ctypes.byref(staging), threads,
+                                         ctypes.byref(out), _stream(stream)))
+    return out
+
+
+def zero_offload_step(plan, rank, contrib, grad_dev, workspace, ws_bytes, master_host, m_host,
+                      v_host, param16_slot_dev, args, dev_result, staging, threads=1,
+                      stream=None):
+    out = zero_step_result_t()
+    _check(lib().zero_offload_step(ctypes.byref(plan), rank, _ptr_array(contrib), _addr(grad_dev),
+                                   _addr(workspace), ws_bytes, _addr(master_host), _addr(m_host),
+                                   _addr(v_host), _addr(param16_slot_dev), ctypes.byref(args),
+                                   _addr(dev_result), ctypes.byref(staging), threads,
+                                   ctypes.byref(out), _stream(stream)))
+    return out
 
 
 def zero_plan_units(numels: Sequence[int], unit_of_tensor: Sequence[int], world_size: int,

@@ -7,10 +7,12 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "host_internal.h"
 #include "zero_internal.h"
 #include "zero_shard.h"
 
-namespace {
+namespace zk {
+namespace host {
 
 thread_local char g_err[512];
 
@@ -133,7 +135,10 @@ int hip_status(int e, const char* what) {
   return fail(ZERO_EHIP, "%s: %s", what, hipGetErrorString((hipError_t)e));
 }
 
-}  // namespace
+}  // namespace host
+}  // namespace zk
+
+using namespace zk::host;
 
 extern "C" {
 

@@ -13,6 +13,7 @@ begin), and guard words on either side catch stray writes.
 from __future__ import annotations
 
 import ctypes
+import os
 from typing import Optional
 
 import numpy as np
@@ -186,4 +187,58 @@ def result_from_bytes(b: bytes) -> abi.zero_step_result_t:
     return abi.zero_step_result_t.from_buffer_copy(b)
 
 
-__all__ = ["DeviceShard", "round_up", "result_from_bytes", "ctypes"]
+__all__ = ["DeviceShard", "OffloadShard", "round_up", "result_from_bytes", "ctypes"]
+
+
+class OffloadShard(DeviceShard):
+    """The offload form of a rank's shard: contributions, g and the fp16 slot
+    on the device; fp32 master, m and v in host memory (numpy arrays); pinned
+    staging for the PCIe pipeline of zero_offload_adam_apply."""
+
+    def __init__(self, w: synth.Workload, rank: int, begin: int = 0, count: Optional[int] = None,
+                 chunk: int = 1 << 22, threads: Optional[int] = None, two_streams: bool = True,
+                 **kw):
+        super().__init__(w, rank, begin, count, **kw)
+        if self.bf16:
+            raise ValueError("the offload form takes fp16 contributions and slots")
+        n = max(self.count, 1)
+        # the device copies of the state are not used here
+        self.master = self.m = self.v = None
+        self.h_master = np.zeros(n, dtype=np.float32)
+        self.h_m = np.zeros(n, dtype=np.float32)
+        self.h_v = np.zeros(n, dtype=np.float32)
+        chunk = round_up(min(chunk, round_up(n, 64)), 64)
+        self.chunk = chunk
+        self._g_pin = torch.empty(2 * chunk, dtype=torch.float32, pin_memory=True)
+        self._h_pin = torch.empty(2 * chunk, dtype=torch.int16, pin_memory=True)
+        # a second stream (default priority) carries the fp16 chunks to the device
+        self.upload_stream = torch.cuda.Stream(self.device) if two_streams else None
+        self.staging = abi.offload_staging(self._g_pin, self._h_pin, chunk, self.upload_stream)
+        self.threads = threads or max(1, len(os.sched_getaffinity(0)))
+
+    def load_initial_state(self):
+        synth.masters(self.w, self.flat_begin, self.count, out=self.h_master[:self.count])
+        self.h_m[:] = 0
+        self.h_v[:] = 0
+        h16 = torch.from_numpy(self.h_master[:self.count].astype(np.float16).view(np.int16))
+        with torch.cuda.stream(self.stream):
+            self.slot.copy_(h16.to(self.device, non_blocking=False))
+        self.stream.synchronize()
+
+    def adam_apply(self, args):
+        return abi.zero_offload_adam_apply(self.plan, self.rank, self.grad, self.h_master, self.h_m,
+                                           self.h_v, self.slot_ptr(), args, self.res,
+                                           self.staging, self.threads, self.stream)
+
+    def step(self, args):
+        return abi.zero_offload_step(self.plan, self.rank, self.contrib_ptrs(), self.grad, self.ws,
+                                     self.ws.numel(), self.h_master, self.h_m, self.h_v,
+                                     self.slot_ptr(), args, self.res, self.staging, self.threads,
+                                     self.stream)
+
+    def fetch(self, name: str, idx=None) -> np.ndarray:
+        host = {"master": self.h_master, "m": self.h_m, "v": self.h_v}.get(name)
+        if host is None:
+            return super().fetch(name, idx)
+        a = host[:self.count]
+        return (a if idx is None else a[np.asarray(idx)]).copy()
