@@ -12,6 +12,8 @@ Every step of each workload runs on the GPU.  The oracle checks:
     random, and around an injected inf), computed one by one by the numpy
     oracle, bit for bit, with the state carried across steps.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -38,6 +40,9 @@ def _sample_indices(w, rank, shard, k=4096):
     idx = set(rng.integers(0, shard, size=k).tolist())
     idx.update(range(0, 32))
     idx.update(range(max(0, shard - 32), shard))
+    for mark in (1 << 30, (1 << 31) - 16):
+        if mark < shard:
+            idx.update(range(mark - 8, min(shard, mark + 9)))
     site = synth.inject_site(w, w.inject_step) if w.inject_step else None
     if site is not None:
         p = orun.workload_plan(w)
@@ -82,6 +87,18 @@ def _feed_and_reduce(dev, step, scale, idx):
     return q_total, bad, cols
 
 
+# The largest shard the ABI accepts (2^31 - 8 elements) at N = 2: element
+# offsets pass 2^31 in the flat buffer and approach it inside the shard; rank
+# 1's shard ends with one padding element.
+_MAX = 0x7FFFFFF8
+MAX_SHARD = dataclasses.replace(
+    synth.TINY, name="max_shard", cfg_id=31, tensors=(("w", (2 * _MAX - 1,)),), world_size=2,
+    sigma=1e-2, loss_scale0=1024.0, weight_decay=0.01, max_grad_norm=1.0, steps=2,
+    other_ranks_from_config=True, parity_ranks=(1,))
+MAX_SHARD_BF16 = dataclasses.replace(MAX_SHARD, name="max_shard_bf16", cfg_id=32, dtype="bf16",
+                                     loss_scale0=1.0, steps=1)
+
+
 def _cases():
     return [pytest.param(w, r, id=f"{w.name}-r{r}") for w, r in (
         (synth.GPT2, 0), (synth.GPT2, 1), (synth.GPT2, 63),
@@ -89,6 +106,7 @@ def _cases():
         (synth.LLAMA3_8B, 0),
         (synth.LLAMA2_70B, 0),
         (synth.LLAMA3_8B_BF16, 0), (synth.LLAMA3_8B_BF16, 7),
+        (MAX_SHARD, 1), (MAX_SHARD_BF16, 1),
     )]
 
 
