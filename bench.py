@@ -176,6 +176,24 @@ def main():
     k1_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / a.steps
     k2_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / a.steps
     ms_per_step = wall * 1e3 / a.steps
+    per_step = sorted(e[0].elapsed_time(e[2]) for e in ev)
+
+    def pct(q):
+        return per_step[min(len(per_step) - 1, int(q * len(per_step)))]
+
+    # a skipped step (another rank overflowed): the reduce runs, the update exits
+    sk = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    sk_args = dev.args(a.warmup + a.steps + 1, w.loss_scale0, other_sq=other_sq,
+                       other_overflow=True)
+    sk[0].record(stream)
+    for _ in range(3):
+        dev.reduce_check(sk_args)
+        dev.adam_apply(sk_args)
+    sk[1].record(stream)
+    torch.cuda.synchronize()
+    if not dev.result().skip:
+        raise RuntimeError("the forced skip was not taken")
+    skip_ms = sk[0].elapsed_time(sk[1]) / 3
 
     b1, b2 = bytes_per_param(n)
     kernels = {
@@ -235,6 +253,9 @@ def main():
                                f"(psi={w.psi}), {w.dtype} contributions and slot, fp32 master/m/v"
                                + (f", {n_units} FSDP units" if w.units else ""),
                    "world_size_simulated": n, "shard": S, "psi": w.psi},
+        "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+        "skipped_step": {"ms": skip_ms, "bytes_per_param": 2 * n + 4,
+                         "gbps": (2 * n + 4) * S / (skip_ms * 1e6)},
         "hbm_gbps_step": (2 * n + 34) * S / (ms_per_step * 1e6),
         "hbm_gbps_step_floor_bytes": (2 * n + 26) * S / (ms_per_step * 1e6),
         "roofline": roofline,
