@@ -178,6 +178,8 @@ def _addr(x) -> int:
     if isinstance(x, int):
         return x
     if hasattr(x, "__array_interface__"):  # numpy array in host memory
+        if not x.flags["C_CONTIGUOUS"]:
+            raise ValueError("host arrays passed to the library must be C-contiguous")
         return int(x.__array_interface__["data"][0])
     return int(x.data_ptr())
 

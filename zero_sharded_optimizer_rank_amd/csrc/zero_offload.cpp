@@ -20,7 +20,9 @@
 #include <string.h>
 
 #include <condition_variable>
+#include <exception>
 #include <functional>
+#include <memory>
 #include <mutex>
 #include <thread>
 #include <vector>
@@ -272,12 +274,16 @@ int zero_host_adam_apply(const float* grad, float* master, float* m, float* v,
   if (count == 0) return ZERO_OK;
   if (!grad || !master || !m || !v || !param16) return fail(ZERO_EINVAL, "NULL array");
   const Coefs k = make_coefs(args, clip_coef);
-  CsrGuard csr;
-  Team team(threads);
-  const std::function<void(int64_t, int64_t)> work = [&](int64_t a, int64_t b) {
-    fn(grad + a, master + a, m + a, v + a, param16 + a, b - a, k);
-  };
-  team.run(count, work);
+  try {
+    CsrGuard csr;
+    Team team(threads);
+    const std::function<void(int64_t, int64_t)> work = [&](int64_t a, int64_t b) {
+      fn(grad + a, master + a, m + a, v + a, param16 + a, b - a, k);
+    };
+    team.run(count, work);
+  } catch (const std::exception& ex) {
+    return fail(ZERO_EINVAL, "host threads: %s", ex.what());
+  }
   return ZERO_OK;
 }
 
@@ -339,7 +345,12 @@ int zero_offload_adam_apply(const zero_plan_t* plan, int32_t rank, const float* 
     return e;
   };
   CsrGuard csr;
-  Team team(threads);
+  std::unique_ptr<Team> team;
+  try {
+    team.reset(new Team(threads));
+  } catch (const std::exception& ex) {
+    return fail(ZERO_EINVAL, "host threads: %s", ex.what());
+  }
   int e = d2h(0);
   for (int64_t i = 0; i < n_chunks && e == hipSuccess; ++i) {
     const int64_t base = i * chunk;
@@ -353,7 +364,7 @@ int zero_offload_adam_apply(const zero_plan_t* plan, int32_t rank, const float* 
     const std::function<void(int64_t, int64_t)> work = [&](int64_t a, int64_t b) {
       fn(g + a, master_host + base + a, m_host + base + a, v_host + base + a, h + a, b - a, k);
     };
-    team.run(len, work);
+    team->run(len, work);
     e = (int)hipMemcpyAsync(param16_slot_dev + base, h, (size_t)len * sizeof(uint16_t),
                             hipMemcpyHostToDevice, up);
     if (e == hipSuccess) e = (int)hipEventRecord(ev.e[2 + (i & 1)], up);
