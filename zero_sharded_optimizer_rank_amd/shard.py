@@ -27,6 +27,8 @@ GUARD = 64  # fp16 guard elements on each side of the slot
 GUARD_WORD = 0x5A5A
 CHUNK = 1 << 25  # elements per host staging chunk
 ROW_ALIGN = 128  # contribution rows start on 256-byte boundaries (whole cache lines)
+STAGGER = 4096  # consecutive buffers of the arena are offset by 4 KiB ...
+STAGGER_PERIOD = 1 << 16  # ... modulo 64 KiB
 
 
 def round_up(x: int, a: int) -> int:
@@ -36,7 +38,7 @@ def round_up(x: int, a: int) -> int:
 class DeviceShard:
     def __init__(self, w: synth.Workload, rank: int, begin: int = 0, count: Optional[int] = None,
                  device: str = "cuda:0", stream: Optional[torch.cuda.Stream] = None,
-                 row_align: int = ROW_ALIGN):
+                 row_align: int = ROW_ALIGN, device_state: bool = True):
         self.w = w
         self.rank = rank
         self.device = torch.device(device)
@@ -58,15 +60,35 @@ class DeviceShard:
         self.stream = stream or torch.cuda.current_stream(self.device)
         ld = round_up(max(count, 1), row_align)
         self.ld = ld
-        self.contrib = torch.empty((n, ld), dtype=torch.int16, device=self.device)
-        self.master = torch.empty(max(count, 1), dtype=torch.float32, device=self.device)
-        self.m = torch.zeros_like(self.master)
-        self.v = torch.zeros_like(self.master)
-        self.grad = torch.empty_like(self.master)
+        # One arena holds every stream of the step.  Consecutive buffers start
+        # 4 KiB apart modulo 64 KiB: with power-of-two-aligned starts the same
+        # element of every stream falls on the same HBM channel interleave and
+        # the multi-stream kernels lose a few percent.
+        e = max(count, 1)
+        self.row_pitch = round_up(2 * ld, STAGGER_PERIOD) + STAGGER
+        st_pitch = round_up(4 * e, STAGGER_PERIOD) + STAGGER
+        n_state = 4 if device_state else 1
+        rows_end = round_up(n * self.row_pitch, STAGGER_PERIOD)
+        slot_elems = GUARD + 8 + count + GUARD
+        slot_at = round_up(rows_end + n_state * st_pitch, STAGGER_PERIOD) + STAGGER
+        self.arena = torch.empty(slot_at + 2 * slot_elems, dtype=torch.uint8, device=self.device)
+        a16 = self.arena.view(torch.int16)
+        self.contrib = a16.as_strided((n, ld), (self.row_pitch // 2, 1), 0)
+
+        def state(k):
+            o = rows_end + k * st_pitch
+            return self.arena[o:o + 4 * e].view(torch.float32)
+        self.grad = state(0)
+        if device_state:
+            self.master, self.m, self.v = state(1), state(2), state(3)
+            self.m.zero_()
+            self.v.zero_()
+        else:
+            self.master = self.m = self.v = None
         # slot with the real buffer's alignment (flat_begin mod 8) plus guards
         self.mis = self.flat_begin % 8
-        self.slot_buf = torch.full((GUARD + 8 + count + GUARD,), GUARD_WORD, dtype=torch.int16,
-                                   device=self.device)
+        self.slot_buf = self.arena[slot_at:slot_at + 2 * slot_elems].view(torch.int16)
+        self.slot_buf.fill_(GUARD_WORD)
         self.slot_off = GUARD + self.mis
         self.ws = torch.zeros(abi.zero_workspace_bytes(self.plan), dtype=torch.uint8,
                               device=self.device)
@@ -86,8 +108,8 @@ class DeviceShard:
         return self.slot_buf.data_ptr() + 2 * self.slot_off
 
     def contrib_ptrs(self):
-        base = self.contrib.data_ptr()
-        return [base + 2 * self.ld * r for r in range(self.w.world_size)]
+        base = self.arena.data_ptr()
+        return [base + self.row_pitch * r for r in range(self.w.world_size)]
 
     def guards_intact(self) -> bool:
         b = self.slot_buf
@@ -198,12 +220,10 @@ class OffloadShard(DeviceShard):
     def __init__(self, w: synth.Workload, rank: int, begin: int = 0, count: Optional[int] = None,
                  chunk: int = 1 << 22, threads: Optional[int] = None, two_streams: bool = True,
                  **kw):
-        super().__init__(w, rank, begin, count, **kw)
+        super().__init__(w, rank, begin, count, device_state=False, **kw)
         if self.bf16:
             raise ValueError("the offload form takes fp16 contributions and slots")
         n = max(self.count, 1)
-        # the device copies of the state are not used here
-        self.master = self.m = self.v = None
         self.h_master = np.zeros(n, dtype=np.float32)
         self.h_m = np.zeros(n, dtype=np.float32)
         self.h_v = np.zeros(n, dtype=np.float32)
