@@ -2,10 +2,10 @@
 unit table in device memory, seeded input feeding, and the one-launch step
 through the C ABI (zero_units_*).
 
-Each unit's buffers are separate allocations, as a real per-unit flat
-parameter would be.  The unit's fp16 slot keeps the alignment it has in the
-unit's flat fp16 buffer (rank * S_u mod 8 elements), with guard words around
-it.  Inputs come from ``synth`` by model element; the element each position
+Each unit has buffers of its own (rows, g, master, m, v, slot), all carved
+from one device arena at staggered starts.  The unit's fp16 slot keeps the
+alignment it has in the unit's flat fp16 buffer (rank * S_u mod 8 elements),
+with guard words around it.  Inputs come from ``synth`` by model element; the element each position
 holds follows the library's own unit plan (zero_plan_units).
 """
 from __future__ import annotations
@@ -18,7 +18,7 @@ import torch
 import synth
 
 from . import abi
-from .shard import GUARD, GUARD_WORD, ROW_ALIGN, round_up
+from .shard import GUARD, GUARD_WORD, ROW_ALIGN, STAGGER, STAGGER_PERIOD, round_up
 
 CHUNK = 1 << 24
 
@@ -38,21 +38,43 @@ class DeviceUnits:
         self.n_units = len(self.infos)
         self.table = abi.unit_table(self.n_units)
         self.bufs: List[dict] = []
+        # One arena for every buffer of every unit; consecutive buffers start
+        # 4 KiB further modulo 64 KiB (as in DeviceShard), and a unit's rows are
+        # spaced by a pitch of 4 KiB modulo 64 KiB.
+        layout, off, k = [], 0, 0
+
+        def place(nbytes):
+            nonlocal off, k
+            at = round_up(off, STAGGER_PERIOD) + (k % 16) * STAGGER
+            off, k = at + nbytes, k + 1
+            return at
+        for info in self.infos:
+            s = info.shard
+            e = max(s, 1)
+            ld = (round_up(2 * round_up(e, ROW_ALIGN), STAGGER_PERIOD) + STAGGER) // 2
+            slot_elems = GUARD + 8 + s + GUARD
+            layout.append((place(2 * ld * n), [place(4 * e) for _ in range(4)],
+                           place(2 * slot_elems), ld, slot_elems))
+        self.arena = torch.zeros(max(round_up(off, 2), 2), dtype=torch.uint8, device=self.device)
+        a16 = self.arena.view(torch.int16)
         for u, info in enumerate(self.infos):
             s = info.shard
-            ld = round_up(max(s, 1), ROW_ALIGN)
+            e = max(s, 1)
+            rows_at, st_at, slot_at, ld, slot_elems = layout[u]
             mis = (rank * s) % 8
+
+            def f32(at):
+                return self.arena[at:at + 4 * e].view(torch.float32)
             b = {
-                # padding columns must read +0; real columns are rewritten every step
-                "contrib": torch.zeros((n, ld), dtype=torch.int16, device=self.device),
-                "grad": torch.empty(max(s, 1), dtype=torch.float32, device=self.device),
-                "master": torch.empty(max(s, 1), dtype=torch.float32, device=self.device),
-                "m": torch.zeros(max(s, 1), dtype=torch.float32, device=self.device),
-                "v": torch.zeros(max(s, 1), dtype=torch.float32, device=self.device),
-                "slot_buf": torch.full((GUARD + 8 + s + GUARD,), GUARD_WORD, dtype=torch.int16,
-                                       device=self.device),
+                # padding columns must read +0 (the arena starts zeroed); real
+                # columns are rewritten every step
+                "contrib": a16.as_strided((n, ld), (ld, 1), rows_at // 2),
+                "grad": f32(st_at[0]), "master": f32(st_at[1]), "m": f32(st_at[2]),
+                "v": f32(st_at[3]),
+                "slot_buf": self.arena[slot_at:slot_at + 2 * slot_elems].view(torch.int16),
                 "slot_off": GUARD + mis, "shard": s, "ld": ld,
             }
+            b["slot_buf"].fill_(GUARD_WORD)
             self.bufs.append(b)
             t = self.table[u]
             t.contrib = b["contrib"].data_ptr()
