@@ -24,6 +24,11 @@
  *     pointers read before the call returns.
  *   - A workspace or result buffer used by one call must not be used by an
  *     overlapping call on another stream.
+ *   - Placement (performance only): the kernels stream several buffers at
+ *     once; buffers whose starts differ by a multiple of 64 KiB put the same
+ *     element of every stream on the same HBM interleave and run a few
+ *     percent slower.  Starting consecutive buffers 4 KiB apart modulo
+ *     64 KiB (odd multiples of 4 KiB between any two) avoids that.
  *
  * The hyperparameters arrive as fp64 and are rounded to fp32 once on the host
  * (1 - beta1 is f32(0.1), not 1f - 0.9f); beta^t is a product of t fp64
@@ -246,7 +251,9 @@ int zero_reduce_adam_step(const zero_plan_t* plan, int32_t rank, const uint16_t*
  *   own_sq = (tree * inv) * inv;  total_sq = own_sq + other_sq
  *   (own_q_lo / own_q_hi are 0; args->other_q must be 0)
  * Arguments, layouts and errors as in the fp16 calls; contribution rows and
- * the slot hold bfloat16 bit patterns.  The workspace is the same size. */
+ * the slot hold bfloat16 bit patterns.  The workspace is the same size.
+ * zero_finalize_bf16 keeps dev_result's own_sq and overflow and recomputes
+ * total_sq, norm, clip_coef and skip from new args. */
 int zero_reduce_check_bf16(const zero_plan_t* plan, int32_t rank, const uint16_t* const* contrib,
                            const zero_step_args_t* args, float* grad_out, void* workspace,
                            size_t ws_bytes, zero_step_result_t* dev_result, hipStream_t stream);
