@@ -284,3 +284,24 @@ def test_workspace_content_does_not_matter(fill):
     print(f"[workspace fill {fill:#x}]", flush=True)
     run_window(synth.LLAMA3_8B, 0, 0, 3_000_001, steps=2, ws_fill=fill)
     run_window(synth.LLAMA3_8B, 0, 0, 3_000_001, steps=2, fused=False, ws_fill=fill)
+
+
+@pytest.mark.parametrize("rank", [0, 2, 3])
+def test_tiny_psi_whole_padding_shard(rank):
+    """psi = 5 over N = 4: S = 2, rank 2 holds one real element and one
+    padding element, rank 3 holds padding only; padding stays exactly zero."""
+    w = dataclasses.replace(synth.TINY, name="psi5", cfg_id=41, tensors=(("a", (5,)),),
+                            world_size=4, max_grad_norm=1.0, weight_decay=0.1)
+    reps = run_window(w, rank, 0, 2, steps=3)
+    assert len(reps) == 3
+    if rank == 3:
+        from zero_sharded_optimizer_rank_amd.shard import DeviceShard
+        d = DeviceShard(w, 3, 0, 2)
+        d.load_initial_state()
+        d.load_contributions(1, w.loss_scale0)
+        d.step(d.args(1, w.loss_scale0))
+        res = d.result()
+        assert res.own_q == 0 and not res.skip
+        for name in ("grad", "master", "m", "v"):
+            assert not np.any(d.fetch(name)), name
+        assert not np.any(d.fetch("slot"))
