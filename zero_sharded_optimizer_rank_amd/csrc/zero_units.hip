@@ -10,12 +10,35 @@
 // workgroup), so a workgroup finds its unit by a binary search and then runs
 // the same per-quad bodies as the flat kernels.  The squared norm and the
 // overflow flag cover all units together; the clip and skip are global.
+#include <stddef.h>
+
 #include "zero_device.h"
 
 namespace zk {
 namespace {
 
 using namespace dev;
+
+// The unit table as the kernels read it: the same layout as
+// zero_unit_buffers_t, with the buffer pointers typed as global memory.  The
+// table's plain pointers would otherwise be generic (flat) addresses, and
+// every access to the unit's buffers would become a FLAT instruction that
+// waits on both memory counters.
+template <typename T>
+using gptr = __attribute__((address_space(1))) T*;
+struct UnitBuffersGlobal {
+  gptr<const uint16_t> contrib;
+  int64_t ld;
+  gptr<float> grad, master, m, v;
+  gptr<uint16_t> param16;
+  int64_t shard, reduce_block, adam_block;
+};
+static_assert(sizeof(UnitBuffersGlobal) == sizeof(zero_unit_buffers_t), "table layout");
+static_assert(offsetof(UnitBuffersGlobal, ld) == offsetof(zero_unit_buffers_t, ld), "ld");
+static_assert(offsetof(UnitBuffersGlobal, param16) == offsetof(zero_unit_buffers_t, param16),
+              "param16");
+static_assert(offsetof(UnitBuffersGlobal, adam_block) ==
+                  offsetof(zero_unit_buffers_t, adam_block), "adam_block");
 
 struct StridedRows {
   const uint16_t* base;
@@ -27,11 +50,26 @@ struct StridedRows {
 // skipped because the next unit starts at the same workgroup).
 template <typename First>
 __device__ __forceinline__ int32_t find_unit(int32_t n_units, int64_t b, First first) {
-  int32_t lo = 0, hi = n_units - 1;
+  int32_t lo = 0, hi = n_units - 1;  // first(lo) <= b always holds (first(0) == 0)
   while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (first(mid) <= b) lo = mid;
-    else hi = mid - 1;
+    const int32_t step = (hi - lo + 7) >> 3;  // >= 1
+    int64_t f[7];
+#pragma unroll
+    for (int k = 0; k < 7; ++k) {
+      const int32_t i = lo + (k + 1) * step;
+      f[k] = i <= hi ? first(i) : INT64_MAX;
+    }
+    int32_t nlo = lo, nhi = hi;
+#pragma unroll
+    for (int k = 0; k < 7; ++k) {
+      const int32_t i = lo + (k + 1) * step;
+      if (i <= hi) {
+        if (f[k] <= b) nlo = i;
+        else if (i - 1 < nhi) nhi = i - 1;
+      }
+    }
+    lo = nlo;
+    hi = nhi < lo ? lo : nhi;
   }
   return lo;
 }
@@ -42,10 +80,10 @@ __global__ __launch_bounds__(ZK_K1_THREADS) void k1u_reduce_check(
   const int64_t b = blockIdx.x;
   if (b == 0 && threadIdx.x == 0) *ticket = 0u;  // arm the finalize kernel's ticket
   const int32_t u = find_unit(n_units, b, [&](int32_t i) { return units[i].reduce_block; });
-  const zero_unit_buffers_t& ub = units[u];
-  const StridedRows rows{ub.contrib, ub.ld};
+  const UnitBuffersGlobal& ub = ((const UnitBuffersGlobal*)units)[u];
+  const StridedRows rows{(const uint16_t*)ub.contrib, ub.ld};
   const int64_t q_first = (b - ub.reduce_block) * ZK_K1_THREADS * ZK_K1_QUADS;
-  const Partial pt = reduce_block(rows, n, ub.shard, q_first, inv32, ub.grad);
+  const Partial pt = reduce_block(rows, n, ub.shard, q_first, inv32, (float*)ub.grad);
   if (threadIdx.x == 0) partials[b] = pt;
 }
 
@@ -56,11 +94,12 @@ __global__ __launch_bounds__(ZK_K2_THREADS) void k2u_adam(
   const float c = res->clip_coef;
   const int64_t b = blockIdx.x;
   const int32_t u = find_unit(n_units, b, [&](int32_t i) { return units[i].adam_block; });
-  const zero_unit_buffers_t& ub = units[u];
+  const UnitBuffersGlobal& ub = ((const UnitBuffersGlobal*)units)[u];
 #pragma unroll
   for (int k = 0; k < ZK_K2_QUADS; ++k) {
     const int64_t qd = ((b - ub.adam_block) * ZK_K2_QUADS + k) * ZK_K2_THREADS + threadIdx.x;
-    adam_quad(ub.grad, ub.master, ub.m, ub.v, ub.param16, ub.shard, qd, c, sc);
+    adam_quad((const float*)ub.grad, (float*)ub.master, (float*)ub.m, (float*)ub.v,
+              (uint16_t*)ub.param16, ub.shard, qd, c, sc);
   }
 }
 

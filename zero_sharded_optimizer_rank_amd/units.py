@@ -38,46 +38,54 @@ class DeviceUnits:
         self.n_units = len(self.infos)
         self.table = abi.unit_table(self.n_units)
         self.bufs: List[dict] = []
-        # One arena for every buffer of every unit; consecutive buffers start
-        # 4 KiB further modulo 64 KiB (as in DeviceShard), and a unit's rows are
-        # spaced by a pitch of 4 KiB modulo 64 KiB.
-        layout, off, k = [], 0, 0
-
-        def place(nbytes):
-            nonlocal off, k
-            at = round_up(off, STAGGER_PERIOD) + (k % 16) * STAGGER
-            off, k = at + nbytes, k + 1
-            return at
-        for info in self.infos:
-            s = info.shard
-            e = max(s, 1)
-            ld = (round_up(2 * round_up(e, ROW_ALIGN), STAGGER_PERIOD) + STAGGER) // 2
-            slot_elems = GUARD + 8 + s + GUARD
-            layout.append((place(2 * ld * n), [place(4 * e) for _ in range(4)],
-                           place(2 * slot_elems), ld, slot_elems))
-        self.arena = torch.zeros(max(round_up(off, 2), 2), dtype=torch.uint8, device=self.device)
+        # One arena, laid out by stream: the contribution rows of all units
+        # side by side (row r of unit u at row r of one wide matrix), then one
+        # region each for g, master, m and v holding every unit's piece, then
+        # the slots.  Each stream of a unit thus sits as far from the unit's
+        # other streams as in the flat layout (a whole rank's worth), and the
+        # regions start 4 KiB apart modulo 64 KiB.  Unit pieces start on
+        # 128-element boundaries.
+        pads = [round_up(max(info.shard, 1), ROW_ALIGN) for info in self.infos]
+        offs = [0]
+        for pd in pads[:-1]:
+            offs.append(offs[-1] + pd)
+        total = max(sum(pads), ROW_ALIGN)
+        row_pitch = round_up(2 * total, STAGGER_PERIOD) + STAGGER
+        ld = row_pitch // 2
+        st_pitch = round_up(4 * total, STAGGER_PERIOD) + STAGGER
+        rows_end = round_up(n * row_pitch, STAGGER_PERIOD)
+        st_at = [rows_end + k * st_pitch for k in range(4)]
+        slots_at = round_up(rows_end + 4 * st_pitch, STAGGER_PERIOD) + STAGGER
+        slot_elems = [GUARD + 8 + info.shard + GUARD for info in self.infos]
+        slot_offs = [0]
+        for se in slot_elems[:-1]:
+            slot_offs.append(slot_offs[-1] + round_up(se, 8))
+        nbytes = slots_at + 2 * (slot_offs[-1] + round_up(slot_elems[-1], 8) if slot_elems else 0)
+        self.arena = torch.zeros(max(nbytes, 2), dtype=torch.uint8, device=self.device)
         a16 = self.arena.view(torch.int16)
+        self.ld = ld
+        self.row_pitch = row_pitch
         for u, info in enumerate(self.infos):
             s = info.shard
             e = max(s, 1)
-            rows_at, st_at, slot_at, ld, slot_elems = layout[u]
             mis = (rank * s) % 8
 
-            def f32(at):
+            def f32(k):
+                at = st_at[k] + 4 * offs[u]
                 return self.arena[at:at + 4 * e].view(torch.float32)
+            sa = slots_at + 2 * slot_offs[u]
             b = {
                 # padding columns must read +0 (the arena starts zeroed); real
                 # columns are rewritten every step
-                "contrib": a16.as_strided((n, ld), (ld, 1), rows_at // 2),
-                "grad": f32(st_at[0]), "master": f32(st_at[1]), "m": f32(st_at[2]),
-                "v": f32(st_at[3]),
-                "slot_buf": self.arena[slot_at:slot_at + 2 * slot_elems].view(torch.int16),
+                "contrib": a16.as_strided((n, pads[u]), (ld, 1), offs[u]),
+                "grad": f32(0), "master": f32(1), "m": f32(2), "v": f32(3),
+                "slot_buf": self.arena[sa:sa + 2 * slot_elems[u]].view(torch.int16),
                 "slot_off": GUARD + mis, "shard": s, "ld": ld,
             }
             b["slot_buf"].fill_(GUARD_WORD)
             self.bufs.append(b)
             t = self.table[u]
-            t.contrib = b["contrib"].data_ptr()
+            t.contrib = self.arena.data_ptr() + 2 * offs[u]
             t.ld = ld
             t.grad, t.master = b["grad"].data_ptr(), b["master"].data_ptr()
             t.m, t.v = b["m"].data_ptr(), b["v"].data_ptr()
