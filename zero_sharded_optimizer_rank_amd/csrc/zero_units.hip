@@ -50,26 +50,11 @@ struct StridedRows {
 // skipped because the next unit starts at the same workgroup).
 template <typename First>
 __device__ __forceinline__ int32_t find_unit(int32_t n_units, int64_t b, First first) {
-  int32_t lo = 0, hi = n_units - 1;  // first(lo) <= b always holds (first(0) == 0)
+  int32_t lo = 0, hi = n_units - 1;
   while (lo < hi) {
-    const int32_t step = (hi - lo + 7) >> 3;  // >= 1
-    int64_t f[7];
-#pragma unroll
-    for (int k = 0; k < 7; ++k) {
-      const int32_t i = lo + (k + 1) * step;
-      f[k] = i <= hi ? first(i) : INT64_MAX;
-    }
-    int32_t nlo = lo, nhi = hi;
-#pragma unroll
-    for (int k = 0; k < 7; ++k) {
-      const int32_t i = lo + (k + 1) * step;
-      if (i <= hi) {
-        if (f[k] <= b) nlo = i;
-        else if (i - 1 < nhi) nhi = i - 1;
-      }
-    }
-    lo = nlo;
-    hi = nhi < lo ? lo : nhi;
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (first(mid) <= b) lo = mid;
+    else hi = mid - 1;
   }
   return lo;
 }
