@@ -41,6 +41,15 @@
 #ifndef ZK_K2_NT_STORE
 #define ZK_K2_NT_STORE 1
 #endif
+// LDS the Adam kernels reserve and never touch, to cap how many of their
+// one-wave workgroups a CU holds: 160 KiB / 14848 B = 11.  With the default
+// 32 waves per CU the eight streams of the update thrash the memory system;
+// measured on the Llama-3-8B shard: 32 waves 5.90 TB/s, 16 waves 6.35,
+// 12 waves 6.44, 11 waves 6.53, 10 waves 6.43, 8 waves 6.21.  (The reduce
+// kernel runs best uncapped.)
+#ifndef ZK_K2_LDS
+#define ZK_K2_LDS 14848
+#endif
 
 namespace zk {
 namespace dev {

@@ -226,7 +226,7 @@ int launch_finalize_bf16(const FinalizeArgs& fa, zero_step_result_t* res, hipStr
 int launch_adam_bf16(const float* grad, float* master, float* m, float* v, uint16_t* slot,
                      int64_t shard, const AdamScalars& sc, const zero_step_result_t* res,
                      hipStream_t stream) {
-  hipLaunchKernelGGL(k2_adam_bf16, dim3((uint32_t)k2_blocks(shard)), dim3(ZK_K2_THREADS), 0,
+  hipLaunchKernelGGL(k2_adam_bf16, dim3((uint32_t)k2_blocks(shard)), dim3(ZK_K2_THREADS), ZK_K2_LDS,
                      stream, grad, master, m, v, slot, shard, sc, res);
   return (int)hipGetLastError();
 }
@@ -234,7 +234,7 @@ int launch_adam_bf16(const float* grad, float* master, float* m, float* v, uint1
 int launch_adam(const float* grad, float* master, float* m, float* v, uint16_t* slot,
                 int64_t shard, const AdamScalars& sc, const zero_step_result_t* res,
                 hipStream_t stream) {
-  hipLaunchKernelGGL(k2_adam, dim3((uint32_t)k2_blocks(shard)), dim3(ZK_K2_THREADS), 0, stream,
+  hipLaunchKernelGGL(k2_adam, dim3((uint32_t)k2_blocks(shard)), dim3(ZK_K2_THREADS), ZK_K2_LDS, stream,
                      grad, master, m, v, slot, shard, sc, res);
   return (int)hipGetLastError();
 }

@@ -100,7 +100,7 @@ int launch_units_reduce(const zero_unit_buffers_t* units_dev, int32_t n_units, i
 
 int launch_units_adam(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
                       const AdamScalars& sc, const zero_step_result_t* res, hipStream_t stream) {
-  hipLaunchKernelGGL(k2u_adam, dim3((uint32_t)blocks), dim3(ZK_K2_THREADS), 0, stream, units_dev,
+  hipLaunchKernelGGL(k2u_adam, dim3((uint32_t)blocks), dim3(ZK_K2_THREADS), ZK_K2_LDS, stream, units_dev,
                      n_units, sc, res);
   return (int)hipGetLastError();
 }
