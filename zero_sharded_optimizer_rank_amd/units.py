@@ -57,10 +57,13 @@ class DeviceUnits:
         st_at = [rows_end + k * st_pitch for k in range(4)]
         slots_at = round_up(rows_end + 4 * st_pitch, STAGGER_PERIOD) + STAGGER
         slot_elems = [GUARD + 8 + info.shard + GUARD for info in self.infos]
+        # each unit's slot buffer starts on a 256-byte boundary, so a slot
+        # with no misalignment (rank * S_u % 8 == 0) covers whole cache lines
         slot_offs = [0]
         for se in slot_elems[:-1]:
-            slot_offs.append(slot_offs[-1] + round_up(se, 8))
-        nbytes = slots_at + 2 * (slot_offs[-1] + round_up(slot_elems[-1], 8) if slot_elems else 0)
+            slot_offs.append(slot_offs[-1] + round_up(se, ROW_ALIGN))
+        nbytes = slots_at + 2 * (slot_offs[-1] + round_up(slot_elems[-1], ROW_ALIGN)
+                                 if slot_elems else 0)
         self.arena = torch.zeros(max(nbytes, 2), dtype=torch.uint8, device=self.device)
         a16 = self.arena.view(torch.int16)
         self.ld = ld
