@@ -166,7 +166,7 @@ typedef struct zero_step_result {
 } zero_step_result_t;
 
 /* Bytes of workspace zero_reduce_check needs for plan->shard elements:
- * 256 + 16 * (256 + ceil(ceil(S / 8) / 256)), about S / 128 bytes; 0 for a
+ * 256 + 16 * (256 + ceil(ceil(S / 4) / 128)), about S / 32 bytes; 0 for a
  * NULL plan or a shard outside 0..ZERO_MAX_SHARD.  The workspace needs no
  * initialisation (the reduce kernel arms its own counter). */
 size_t zero_workspace_bytes(const zero_plan_t* plan);

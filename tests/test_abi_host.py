@@ -102,8 +102,8 @@ def test_host_argument_errors():
     assert abi.zero_plan_real(plan, 5) == -1
     for shard in (0, 1, 8, 2048, 2049, 10**9):
         p = abi.zero_plan_t(shard, 1, 1, shard, shard)
-        groups = -(-shard // 8)
-        assert abi.zero_workspace_bytes(p) == 256 + 16 * (256 + max(1, -(-groups // 256)))
+        quads = -(-shard // 4)  # one reduce workgroup per 128 quads
+        assert abi.zero_workspace_bytes(p) == 256 + 16 * (256 + max(1, -(-quads // 128)))
     assert abi.zero_workspace_bytes(abi.zero_plan_t(0, 1, 1, -1, -1)) == 0
     assert abi.RESULT_BYTES == 56
 
@@ -150,7 +150,7 @@ def test_units_prepare_layout_and_errors():
         t.ld = -(-max(s, 1) // 8) * 8
         t.shard = s
     b1, b2 = abi.zero_units_prepare(tab, len(shards))
-    k1 = [max(1, -(-(-(-s // 4)) // 512)) for s in shards]
+    k1 = [max(1, -(-(-(-s // 4)) // 128)) for s in shards]  # 128 quads per reduce workgroup
     k2 = [-(-(-(-s // 4)) // 64) if s else 0 for s in shards]
     assert b1 == sum(k1) and b2 == sum(k2)
     assert [tab[i].reduce_block for i in range(len(shards))] == [sum(k1[:i]) for i in range(5)]

@@ -24,7 +24,7 @@
 #define ZK_K2_QUADS 1  // 4-element quads per Adam thread
 #endif
 #ifndef ZK_K1_THREADS
-#define ZK_K1_THREADS 512  // threads per reduce workgroup (a multiple of 64)
+#define ZK_K1_THREADS 128  // threads per reduce workgroup (a multiple of 64)
 #endif
 #ifndef ZK_K2_THREADS
 #define ZK_K2_THREADS 64  // threads per Adam workgroup
@@ -50,9 +50,25 @@
 #ifndef ZK_K2_LDS
 #define ZK_K2_LDS 14848
 #endif
+// The reduce kernel is capped the same way, by N: with 128-thread (two-wave)
+// workgroups, 16 per CU for N <= 8 and 12 per CU beyond (10240 and 13312 B
+// of reserved LDS).  Measured reduce rates, cap 10 / 12 / 14 / 16 / none:
+// N = 8:  5.65 / 6.24 / 6.51 / 6.51 / 6.05 TB/s;  N = 16: 6.21 / 6.39 /
+// 6.21 / 6.20 / 6.09;  N = 32: 6.20 / 6.22 / 6.03 / 6.01 / 5.93;  N = 64:
+// 6.26 / 6.20 / 5.99 / 6.00 / 5.94 (the earlier 512-thread, 8-row-batch
+// form: 6.23, 5.66, 5.56, 5.77).
+#ifndef ZK_K1_LDS_SMALL_N
+#define ZK_K1_LDS_SMALL_N 10240
+#endif
+#ifndef ZK_K1_LDS
+#define ZK_K1_LDS 13312
+#endif
 
 namespace zk {
 namespace dev {
+
+// Reserved LDS of a reduce launch over n contribution rows.
+inline unsigned k1_lds(int n) { return n <= 8 ? ZK_K1_LDS_SMALL_N : ZK_K1_LDS; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -65,7 +81,7 @@ struct Partial {
 };
 static_assert(sizeof(Partial) == kPartialBytes, "partial layout");
 
-constexpr int kRankBatch = 8;  // contribution rows loaded before they are summed
+constexpr int kRankBatch = 4;  // contribution rows loaded before they are summed
 
 template <bool NT, typename T>
 __device__ __forceinline__ T vload(const T* p) {
@@ -552,7 +568,7 @@ __device__ inline void finalize_bf16_into(double tree, uint32_t bad, const Final
   res->reserved = 0;
 }
 
-constexpr int kTreeChunk = 4096;  // most partials one workgroup of the tree kernel sums
+constexpr int kTreeChunk = 16384;  // most partials one workgroup of the tree kernel sums
 
 // LDS tree over `count` values (count a power of two, <= kTreeChunk) held in
 // s[0..count); the result lands in s[0].

@@ -172,7 +172,7 @@ int launch_reduce_check(const uint16_t* const* contrib, int n, int64_t shard, fl
   ContribTable ct;
   for (int r = 0; r < ZERO_MAX_RANKS; ++r) ct.p[r] = r < n ? contrib[r] : nullptr;
   const int64_t blocks = k1_blocks(shard);
-  hipLaunchKernelGGL(k1_reduce_check, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), 0, stream, ct,
+  hipLaunchKernelGGL(k1_reduce_check, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), k1_lds(n), stream, ct,
                      n, shard, inv32, grad, (Partial*)workspace_partials(workspace),
                      (uint32_t*)workspace);
   const int e = (int)hipGetLastError();
@@ -203,7 +203,7 @@ int launch_reduce_check_bf16(const uint16_t* const* contrib, int n, int64_t shar
   uint32_t* ticket = (uint32_t*)workspace;
   Partial* level2 = (Partial*)((char*)workspace + kTicketBytes);
   Partial* partials = (Partial*)workspace_partials(workspace);
-  hipLaunchKernelGGL(k1_reduce_check_bf16, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), 0, stream,
+  hipLaunchKernelGGL(k1_reduce_check_bf16, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), k1_lds(n), stream,
                      ct, n, shard, inv32, grad, partials, ticket);
   int e = (int)hipGetLastError();
   if (e != hipSuccess) return e;

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(ZK_K2_THREADS) void k2u_adam(
 
 int launch_units_reduce(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
                         int n, float inv32, void* workspace, hipStream_t stream) {
-  hipLaunchKernelGGL(k1u_reduce_check, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), 0, stream,
+  hipLaunchKernelGGL(k1u_reduce_check, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), k1_lds(n), stream,
                      units_dev, n_units, n, inv32, (Partial*)workspace_partials(workspace),
                      (uint32_t*)workspace);
   return (int)hipGetLastError();
