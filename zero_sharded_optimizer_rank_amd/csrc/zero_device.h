@@ -63,6 +63,13 @@
 #ifndef ZK_K1_LDS
 #define ZK_K1_LDS 13312
 #endif
+// The bf16 reduce kernel (longer-lived waves: fp64 squares and a shuffle
+// tree per quad) runs best at 12 workgroups per CU for every N; at N = 8,
+// cap 8 / 10 / 11 / 12 / 13 / 14 / 16 / none: 5.31 / 6.06 / 6.35 / 6.61 /
+// 6.38 / 6.07 / 6.07 / 5.97 TB/s.
+#ifndef ZK_K1B_LDS
+#define ZK_K1B_LDS 13312
+#endif
 
 namespace zk {
 namespace dev {

@@ -203,7 +203,7 @@ int launch_reduce_check_bf16(const uint16_t* const* contrib, int n, int64_t shar
   uint32_t* ticket = (uint32_t*)workspace;
   Partial* level2 = (Partial*)((char*)workspace + kTicketBytes);
   Partial* partials = (Partial*)workspace_partials(workspace);
-  hipLaunchKernelGGL(k1_reduce_check_bf16, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), k1_lds(n), stream,
+  hipLaunchKernelGGL(k1_reduce_check_bf16, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), ZK_K1B_LDS, stream,
                      ct, n, shard, inv32, grad, partials, ticket);
   int e = (int)hipGetLastError();
   if (e != hipSuccess) return e;
