@@ -24,6 +24,9 @@
  *     pointers read before the call returns.
  *   - A workspace or result buffer used by one call must not be used by an
  *     overlapping call on another stream.
+ *   - The buffers passed to one call must not overlap one another (the
+ *     kernels read and write them as distinct memory); only the in-place
+ *     state arrays (master, m, v) are read and written by the same call.
  *   - Placement (performance only): the kernels stream several buffers at
  *     once; buffers whose starts differ by a multiple of 64 KiB put the same
  *     element of every stream on the same HBM interleave and run a few
