@@ -246,3 +246,12 @@ def test_bf16_empty_shard_and_errors():
     with pytest.raises(abi.ZeroError) as e:
         abi.zero_finalize_bf16(plan, bad, res)
     assert e.value.code == abi.ZERO_EINVAL
+
+
+@pytest.mark.parametrize("count", [512 * 256 - 1, 512 * 256 + 1, 512 * 512 + 3, 512 * 256 * 3 + 7])
+def test_bf16_tree_chunk_boundaries(count):
+    """Window sizes around the tree kernel's chunk transitions (one partial
+    per 512-element workgroup, at most 256 tree workgroups, power-of-two
+    chunks): the value is the one fixed tree whatever the split."""
+    print(f"[bf16 tree chunks count {count}]", flush=True)
+    run_window(synth.LLAMA3_8B_BF16, 1, 4097, count, steps=2)
