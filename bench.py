@@ -113,7 +113,8 @@ def main():
                     help="time the offload form: reduce on the GPU, Adam on the host from "
                          "host-resident state, fp16 parameters back over PCIe")
     ap.add_argument("--threads", type=int, default=0,
-                    help="host threads of the offload form (0: the CPUs this process may use)")
+                    help="host threads of the offload form (0: up to 8 of the CPUs this "
+                         "process may use)")
     ap.add_argument("--one-stream", action="store_true",
                     help="offload form: both PCIe directions on one stream")
     ap.add_argument("--calib-bytes", type=float, default=4e9,
