@@ -158,17 +158,16 @@ AdamFn pick(int32_t vector_width) {
 class Team {
  public:
   explicit Team(int threads) : n_threads_(threads) {
-    for (int t = 1; t < threads; ++t) workers_.emplace_back([this, t] { loop(t); });
-  }
-  ~Team() {
-    {
-      std::lock_guard<std::mutex> lk(mu_);
-      quit_ = true;
-      ++gen_;
+    try {
+      for (int t = 1; t < threads; ++t) workers_.emplace_back([this, t] { loop(t); });
+    } catch (...) {
+      // a thread failed to start: stop and join the ones that did before the
+      // exception leaves (a joinable std::thread must not be destroyed)
+      stop();
+      throw;
     }
-    cv_.notify_all();
-    for (auto& w : workers_) w.join();
   }
+  ~Team() { stop(); }
   void run(int64_t n, const std::function<void(int64_t, int64_t)>& fn) {
     {
       std::lock_guard<std::mutex> lk(mu_);
@@ -184,6 +183,17 @@ class Team {
   }
 
  private:
+  void stop() {
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      quit_ = true;
+      ++gen_;
+    }
+    cv_.notify_all();
+    for (auto& w : workers_)
+      if (w.joinable()) w.join();
+    workers_.clear();
+  }
   void slice(int t) {
     const int64_t per = ((n_ + n_threads_ - 1) / n_threads_ + 63) / 64 * 64;
     const int64_t a = per * t;
