@@ -66,6 +66,26 @@ def test_host_adam_matches_oracle(count, threads):
                 assert np.array_equal(_bits(got), _bits(exp.view(got.dtype))), (width, coef)
 
 
+@pytest.mark.parametrize("step", [38_000, 1_000_000])
+def test_host_adam_late_step_bias_corrections(step):
+    """At late steps both beta powers fall below 2^-54, where 1 - beta^t is
+    exactly 1 in fp64: the host stops the power loop there, the oracle runs
+    all t products, and the updates must still agree bit for bit."""
+    _lib_or_skip()
+    rng = np.random.default_rng(step)
+    n = 257
+    g = rng.standard_normal(n).astype(np.float32)
+    p = rng.standard_normal(n).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    v = (rng.random(n) * 1e-3).astype(np.float32)
+    want = _oracle(g, p, m, v, 3e-4, 0.1, step, 1.0)
+    pp, mm, vv = p.copy(), m.copy(), v.copy()
+    h = np.zeros(n, np.uint16)
+    abi.zero_host_adam_apply(g, pp, mm, vv, h, n, _args(lr=3e-4, step=step), 1.0, 1, 1)
+    for got, exp in zip((pp, mm, vv, h), want):
+        assert np.array_equal(_bits(got), _bits(exp.view(got.dtype)))
+
+
 def test_host_adam_subnormals_and_extremes():
     _lib_or_skip()
     g = np.array([1e-45, -1e-45, 1e-40, 3e38, -3e38, 0.0, -0.0, 2.0**-126, 1e-20, 65504.0],

@@ -78,10 +78,13 @@ zk::FinalizeArgs finalize_args(const zero_plan_t* plan, const zero_step_args_t* 
 }
 
 // Coefficients in fp64 from the decimal hyperparameters, each rounded to fp32
-// once; beta^t as t left-to-right fp64 products.
+// once; beta^t as t left-to-right fp64 products.  Once both powers are at or
+// below 2^-54, 1 - p rounds to exactly 1 (a tie at 2^-54 goes to the even 1),
+// and further products only shrink them, so the loop stops there.
 zk::AdamScalars adam_scalars(const zero_step_args_t* a) {
   double p1 = a->beta1, p2 = a->beta2;
   for (int64_t i = 1; i < a->step; ++i) {
+    if (p1 <= 0x1p-54 && p2 <= 0x1p-54) break;
     p1 *= a->beta1;
     p2 *= a->beta2;
   }
