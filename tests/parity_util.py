@@ -147,3 +147,67 @@ def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Opti
             o_t += 1
         assert scaler.t == o_t
     return reports
+
+
+def run_units_all_ranks(w: synth.Workload, max_norm: Optional[float] = None) -> List[StepReport]:
+    """Every rank of a unit layout on the GPU (zero_units_* through DeviceUnits)
+    and in the oracle, all steps, with the exact all-reduce of the squared-norm
+    integers and overflow flags between the ranks; every rank's g, result and
+    state compared bit for bit.  Returns rank 0's reports."""
+    import zero_sharded_optimizer_rank_amd.abi as abi
+    from zero_sharded_optimizer_rank_amd.units import DeviceUnits
+
+    max_norm = w.max_grad_norm if max_norm is None else max_norm
+    n = w.world_size
+    up = orun.workload_unit_plan(w)
+    devs = [DeviceUnits(w, r) for r in range(n)]
+    for d in devs:
+        d.load_initial_state()
+    ost = [list(orun.unit_rank_initial_state(w, up, r)) for r in range(n)]
+    ost = [[s[0], s[1], s[2], s[3].view(np.uint16)] for s in ost]
+    scaler = abi.new_scaler(w.loss_scale0)
+    o_scale, o_good, o_t = w.loss_scale0, 0, 0
+    flat_plan = abi.zero_plan_t(0, n, 1, 0, 0)
+    reports = []
+    for step in range(1, w.steps + 1):
+        for d in devs:
+            d.load_contributions(step, scaler.scale)
+        base = devs[0].args(scaler.t + 1, scaler.scale, max_norm=max_norm)
+        for d in devs:
+            d.reduce_check(base)
+        rs = [d.result() for d in devs]
+        for r, d in enumerate(devs):
+            a = d.args(scaler.t + 1, scaler.scale, max_norm=max_norm,
+                       other_q=sum(rs[x].own_q for x in range(n) if x != r),
+                       other_overflow=any(rs[x].overflow for x in range(n) if x != r))
+            abi.zero_finalize(flat_plan, a, d.res, d.stream)
+            d.adam_apply(a)
+        # oracle
+        sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, o_t + 1, n, o_scale)
+        accs = [oracle.reduce_contributions(orun.unit_rank_contrib(w, up, r, step, o_scale))
+                for r in range(n)]
+        qs = [oracle.exact_sq_units(x) for x in accs]
+        bads = [oracle.nonfinite(x) for x in accs]
+        skipped = None
+        for r, d in enumerate(devs):
+            fin = oracle.finalize(qs[r], bads[r], sc.inv64, max_norm,
+                                  other_q=sum(qs) - qs[r],
+                                  other_overflow=any(bads[x] for x in range(n) if x != r))
+            check_result(d.result(), fin, step)
+            skipped = fin.skip
+            g = oracle.unscale(accs[r], sc.inv32)
+            assert np.array_equal(d.fetch("grad").view(np.uint32), g.view(np.uint32)), (step, r)
+            if not fin.skip:
+                p, m, v, h = oracle.adam_apply(g, ost[r][0], ost[r][1], ost[r][2], sc, fin.coef)
+                ost[r] = [p, m, v, h.view(np.uint16)]
+            rep = StepReport(step, fin.skip, float(fin.coef))
+            for name, k in (("master", 0), ("m", 1), ("v", 2), ("slot", 3)):
+                compare_state(rep, name, d.fetch(name), ost[r][k])
+            assert all(x == 0 for x in rep.mismatches.values()), (step, r, rep.mismatches)
+            assert d.guards_intact(), (step, r)
+            if r == 0:
+                reports.append(rep)
+        abi.zero_scaler_update(scaler, skipped)
+        o_scale, o_good = oracle.scaler_update(o_scale, o_good, skipped)
+        o_t += 0 if skipped else 1
+    return reports
