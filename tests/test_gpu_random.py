@@ -126,3 +126,22 @@ def test_random_unit_layout_matches_oracle(seed):
           f"scale={w.loss_scale0} sigma={w.sigma} clip={w.max_grad_norm} "
           f"inject={w.inject_step}", flush=True)
     run_units_all_ranks(w)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_configuration_offload_matches_oracle(seed):
+    """The offload form (reduce on the GPU, Adam on the host, fp16 back over
+    PCIe) on random fp16 configurations, with a random pipeline chunk and
+    thread count."""
+    w = random_workload(100 + seed)
+    if w.dtype != "fp16":
+        w = dataclasses.replace(w, dtype="fp16", loss_scale0=1024.0)
+    p = orun.workload_plan(w)
+    rng = np.random.default_rng([0x7A40, seed])
+    chunk = int(_pick(rng, [64, 192, 4096, 1 << 16]))
+    threads = int(_pick(rng, [1, 2, 5, 8]))
+    for rank in w.parity_ranks:
+        print(f"[random offload {seed}] N={w.world_size} S={p.shard} rank={rank} chunk={chunk} "
+              f"threads={threads} scale={w.loss_scale0} clip={w.max_grad_norm} "
+              f"inject={w.inject_step}", flush=True)
+        run_window(w, rank, 0, p.shard, offload=dict(chunk=chunk, threads=threads))
