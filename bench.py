@@ -95,6 +95,38 @@ def cpu_baseline(w, seconds: float):
                       f"{reps} oracle steps (numpy, one thread), {el:.1f} s"}
 
 
+def calibration_copy(nbytes: float, stream):
+    """Time a one-shot copy of known size (measurement-only library): the
+    ceiling a streaming kernel reaches on this part, and the known-size kernel
+    the counter passes are scaled by.  The caller frees its buffers first."""
+    if nbytes <= 0:
+        return None
+    import ctypes
+    import torch
+    from zero_sharded_optimizer_rank_amd.build import CALIB_LIB
+    cl = ctypes.CDLL(CALIB_LIB)
+    cl.zero_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_int, ctypes.c_void_p]
+    nb = int(nbytes) // 16 * 16
+    torch.cuda.empty_cache()
+    src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    best = None
+    for threads in (64, 256):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for rep in range(4):
+            if rep == 1:
+                e0.record(stream)
+            rc = cl.zero_calib_copy(src.data_ptr(), dst.data_ptr(), nb, threads,
+                                    stream.cuda_stream)
+            assert rc == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gbps = 2 * nb * 3 / (e0.elapsed_time(e1) * 1e6)
+        best = gbps if best is None else max(best, gbps)
+    return {"copy_gbps": best, "bytes": nb}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +149,12 @@ def main():
                          "process may use)")
     ap.add_argument("--one-stream", action="store_true",
                     help="offload form: both PCIe directions on one stream")
+    ap.add_argument("--one-pass", action="store_true",
+                    help="time zero_reduce_adam_step_1pass (steps without clipping: reduce and "
+                         "update in one pass into a second state set, 2N + 26 bytes per element)")
+    ap.add_argument("--no-clip", action="store_true",
+                    help="turn the workload's gradient clipping off (a variant, named in the "
+                         "config; needed for --one-pass on workloads that clip)")
     ap.add_argument("--calib-bytes", type=float, default=4e9,
                     help="bytes of the calibration copy timed next to the step (0: skip)")
     a = ap.parse_args()
@@ -133,8 +171,13 @@ def main():
 
     abi.lib()
     w = synth.BY_NAME[a.workload]
+    if a.no_clip:
+        import dataclasses
+        w = dataclasses.replace(w, max_grad_norm=0.0)
     if a.offload:
         return offload_main(a, w)
+    if a.one_pass:
+        return one_pass_main(a, w)
     if w.units is not None:
         from zero_sharded_optimizer_rank_amd.units import DeviceUnits
         dev = DeviceUnits(w, a.rank)
@@ -216,36 +259,13 @@ def main():
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": kernels[dom]["gbps"] / HBM_PEAK_GBPS, "traffic": traffic}
 
-    calib = None
-    if a.calib_bytes > 0:
-        import ctypes
-        from zero_sharded_optimizer_rank_amd.build import CALIB_LIB
-        cl = ctypes.CDLL(CALIB_LIB)
-        cl.zero_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                       ctypes.c_int, ctypes.c_void_p]
-        nb = int(a.calib_bytes) // 16 * 16
-        del dev
-        torch.cuda.empty_cache()
-        src = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        dst = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        best = None
-        for threads in (64, 256):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            for rep in range(4):
-                if rep == 1:
-                    e0.record(stream)
-                rc = cl.zero_calib_copy(src.data_ptr(), dst.data_ptr(), nb, threads,
-                                        stream.cuda_stream)
-                assert rc == 0
-            e1.record(stream)
-            torch.cuda.synchronize()
-            gbps = 2 * nb * 3 / (e0.elapsed_time(e1) * 1e6)
-            best = gbps if best is None else max(best, gbps)
-        calib = {"copy_gbps": best, "bytes": nb}
+    del dev
+    calib = calibration_copy(a.calib_bytes, stream)
 
     out = {
         "metric": "params updated/sec + achieved HBM GB/s, Llama-3-8B shard step N=8"
-        if w.name == "llama3_8b" else f"params updated/sec + achieved HBM GB/s, {w.name} shard step",
+        if w.name == "llama3_8b" and not a.no_clip
+        else f"params updated/sec + achieved HBM GB/s, {w.name} shard step",
         "value": real / (ms_per_step / 1e3),
         "unit": "params/s",
         "n_gpus": 1,
@@ -259,7 +279,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: rank {a.rank} of N={n}, shard S={S} "
                                f"(psi={w.psi}), {w.dtype} contributions and slot, fp32 master/m/v"
-                               + (f", {n_units} FSDP units" if w.units else ""),
+                               + (f", {n_units} FSDP units" if w.units else "")
+                               + (", clipping turned off" if a.no_clip else ""),
                    "world_size_simulated": n, "shard": S, "psi": w.psi},
         "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         "skipped_step": skipped,
@@ -273,6 +294,78 @@ def main():
     }
     if not a.no_cpu_baseline and w.units is None:
         out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def one_pass_main(a, w):
+    """One JSON line for the single-pass step (steps without clipping)."""
+    import torch
+    from zero_sharded_optimizer_rank_amd import abi
+    from zero_sharded_optimizer_rank_amd.shard import DeviceShard
+
+    if w.max_grad_norm > 0 or w.dtype != "fp16" or w.units is not None:
+        print("--one-pass takes a flat fp16 workload without clipping (add --no-clip to turn "
+              "a workload's clipping off)", file=sys.stderr)
+        sys.exit(2)
+    dev = DeviceShard(w, a.rank, one_pass=True)
+    real = abi.zero_plan_real(dev.full_plan, a.rank)
+    S, n, stream = dev.count, w.world_size, dev.stream
+    other_sq = w.other_sq(real) if w.other_ranks_from_config else 0.0
+    t_setup = time.perf_counter()
+    dev.load_initial_state()
+    dev.load_contributions(1, w.loss_scale0)
+    setup_s = time.perf_counter() - t_setup
+    # one result word per timed step, checked after the timed region: every
+    # step must have applied, so adopting each new set unconditionally is right
+    res = torch.zeros((a.warmup + a.steps, abi.RESULT_BYTES), dtype=torch.uint8,
+                      device=dev.device)
+    for i in range(a.warmup):
+        dev.step_1pass(dev.args(i + 1, w.loss_scale0, other_sq=other_sq), res=res[i])
+        dev.adopt()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        ev[i][0].record(stream)
+        dev.step_1pass(dev.args(a.warmup + i + 1, w.loss_scale0, other_sq=other_sq),
+                       res=res[a.warmup + i])
+        ev[i][1].record(stream)
+        dev.adopt()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    raw = res.cpu().numpy()
+    if any(abi.zero_step_result_t.from_buffer_copy(raw[i].tobytes()).skip
+           for i in range(raw.shape[0])):
+        raise RuntimeError("a step was skipped")
+    ms = wall * 1e3 / a.steps
+    k_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / a.steps
+    per_step = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    del dev
+    calib = calibration_copy(a.calib_bytes, stream)
+    bpp = 2 * n + 26
+    gbps = bpp * S / (k_ms * 1e6)
+    out = {
+        "metric": f"params updated/sec + achieved HBM GB/s, {w.name} shard step, single pass",
+        "value": real / (ms / 1e3), "unit": "params/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name}: rank {a.rank} of N={n}, shard S={S} (psi={w.psi}), "
+                               f"fp16 contributions and slot, fp32 master/m/v in two sets, "
+                               f"single-pass step"
+                               + (" (clipping turned off)" if a.no_clip else " (no clipping)"),
+                   "world_size_simulated": n, "shard": S, "psi": w.psi},
+        "step_ms_p10_p50_p90": [per_step[int(q * (len(per_step) - 1))] for q in (0.1, 0.5, 0.9)],
+        "hbm_gbps_step": bpp * S / (ms * 1e6),
+        "roofline": {"bound": "hbm", "kernel": "k12_reduce_adam", "achieved": gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic_for(w.name + "_1pass", "k12_reduce_adam")},
+        "kernels": {"k12_reduce_adam": {"ms": k_ms, "bytes_per_param": bpp, "bytes": bpp * S,
+                                        "gbps": gbps,
+                                        "note": "event pair spans the pass and the finalize"}},
+        "calibration_copy": calib,
+        "setup_s": setup_s,
+        "kernel_hash": kernel_hash(),
+    }
     print(json.dumps(out), flush=True)
 
 

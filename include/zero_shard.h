@@ -243,6 +243,42 @@ int zero_reduce_adam_step(const zero_plan_t* plan, int32_t rank, const uint16_t*
                           const zero_step_args_t* args, zero_step_result_t* dev_result,
                           hipStream_t stream);
 
+/*
+ * zero_reduce_adam_step_1pass: the whole step in one streaming pass, for steps
+ * without gradient clipping (args->max_grad_norm <= 0), such as the GPT-2 and
+ * small workloads whose configurations clip nothing.  Pages: as
+ * zero_reduce_check and zero_adam_apply; the tutorial's loss scaling (§4.3)
+ * supplies the only global dependency left, the skip on overflow.
+ * Without clipping, no element's update depends on the shard's norm, only on
+ * whether any rank overflowed.  So one kernel reduces the contributions, adds
+ * the exact squares to the partial sums and applies the update (clip
+ * coefficient 1) from the `in` state into a second, distinct `out` state and
+ * slot; the finalize then writes dev_result as zero_reduce_check does.  The
+ * gradient is never written: the step moves 2N + 26 bytes per element instead
+ * of 2N + 34.
+ *   contrib, workspace, ws_bytes, dev_result   as zero_reduce_check
+ *   master_in, m_in, v_in     device [S] fp32, 16-byte aligned, read only
+ *   master_out, m_out, v_out  device [S] fp32, 16-byte aligned, written
+ *   param16_slot_out          device [S] fp16 bit patterns, 2-byte aligned
+ *                             (a second flat buffer's slot at rank * S)
+ *   args                      as zero_reduce_adam_step; max_grad_norm <= 0
+ * Results: when dev_result->skip is 0 the out state and slot hold exactly what
+ * zero_reduce_adam_step would have left in master, m, v and the slot (the
+ * caller adopts them, e.g. by swapping buffer sets); when it is 1 they hold
+ * unspecified values and the in state is the unchanged state (the caller
+ * keeps it and its slot).  dev_result is bit-identical to zero_reduce_check's
+ * with clip_coef 1.
+ * Errors: as zero_reduce_adam_step, plus ZERO_EINVAL for max_grad_norm > 0,
+ * for an out buffer that overlaps an in buffer, and for out buffers that
+ * overlap one another.  Nothing is launched if a check fails.
+ */
+int zero_reduce_adam_step_1pass(const zero_plan_t* plan, int32_t rank,
+                                const uint16_t* const* contrib, const float* master_in,
+                                const float* m_in, const float* v_in, float* master_out,
+                                float* m_out, float* v_out, uint16_t* param16_slot_out,
+                                void* workspace, size_t ws_bytes, const zero_step_args_t* args,
+                                zero_step_result_t* dev_result, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* bf16 variant: bfloat16 gradient contributions and parameter slot, no loss
  * scaling needed (the tutorial's §4.3 suggests bf16 where the hardware has it,

@@ -84,11 +84,14 @@ def other_overflow_at(w: synth.Workload, step: int, flat_begin: int, count: int)
 
 def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Optional[int] = None,
                fused: bool = True, strict: bool = True,
-               ws_fill: Optional[int] = None, offload: Optional[dict] = None) -> List[StepReport]:
+               ws_fill: Optional[int] = None, offload: Optional[dict] = None,
+               one_pass: bool = False) -> List[StepReport]:
     """Run `steps` steps of the workload on one window of rank's shard on the
     GPU and in the oracle; compare every step.  With `offload` (OffloadShard
     keyword arguments) the update runs in the offload form: host state, PCIe
-    pipeline."""
+    pipeline.  With `one_pass` (unclipped workloads) each step is
+    zero_reduce_adam_step_1pass into the second state set, adopted only when
+    the step was not skipped; no gradient is written, so none is compared."""
     import zero_sharded_optimizer_rank_amd.abi as abi
     from zero_sharded_optimizer_rank_amd.shard import DeviceShard, OffloadShard
 
@@ -96,7 +99,7 @@ def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Opti
     if offload is not None:
         dev = OffloadShard(w, rank, begin, count, **offload)
     else:
-        dev = DeviceShard(w, rank, begin, count)
+        dev = DeviceShard(w, rank, begin, count, one_pass=one_pass)
     dev.load_initial_state()
     p = orun.workload_plan(w)
     flat_begin = rank * p.shard + begin
@@ -115,12 +118,16 @@ def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Opti
             dev.ws.fill_(ws_fill)  # the workspace needs no initialisation
         dev.load_contributions(step, scaler.scale)
         args = dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq, other_overflow=ovf_other)
-        if fused:
+        if one_pass:
+            dev.step_1pass(args)
+        elif fused:
             dev.step(args)
         else:
             dev.reduce_check(args)
             dev.adam_apply(args)
         res = dev.result()
+        if one_pass and not res.skip:
+            dev.adopt()
         # oracle
         c = orun.shard_contrib(w, p, rank, step, o_scale, begin, count)
         sc = oracle.step_scalars(w.lr, w.betas[0], w.betas[1], w.eps, w.weight_decay, o_t + 1,
@@ -130,9 +137,11 @@ def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Opti
                       other_overflow=ovf_other)
         check_result(res, out.fin, step)
         rep = StepReport(step, out.fin.skip, float(out.fin.coef))
-        g = dev.fetch("grad")
-        rep.mismatches["grad"] = int(np.count_nonzero(g.view(np.uint32) != out.g.view(np.uint32)))
-        assert rep.mismatches["grad"] == 0, (step, "grad")
+        if not one_pass:
+            g = dev.fetch("grad")
+            rep.mismatches["grad"] = int(np.count_nonzero(g.view(np.uint32) !=
+                                                          out.g.view(np.uint32)))
+            assert rep.mismatches["grad"] == 0, (step, "grad")
         op, om, ov = out.p, out.m, out.v
         oh = out.h.view(np.uint16)
         for name, want in (("master", op), ("m", om), ("v", ov), ("slot", oh)):

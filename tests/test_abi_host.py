@@ -169,3 +169,34 @@ def test_units_prepare_layout_and_errors():
     abi.zero_units_prepare(tab, len(shards))
     tab[4].adam_block += 1  # a stale table is refused
     assert abi.zero_units_workspace_bytes(tab, len(shards)) == 0
+
+
+def test_one_pass_argument_checks_without_launching():
+    """zero_reduce_adam_step_1pass rejects clipping and overlapping in / out
+    state before anything reaches the GPU (the pointers here are never used)."""
+    abi = _abi()
+    S = 1000
+    plan = abi.zero_plan_t(S, 2, 1, S, 2 * S)
+    base = 1 << 32
+    rows = [base, base + (1 << 20)]
+    ins = [base + (2 << 20), base + (3 << 20), base + (4 << 20)]
+    outs = [base + (5 << 20), base + (6 << 20), base + (7 << 20)]
+    slot = base + (8 << 20)
+    ws_bytes = abi.zero_workspace_bytes(plan)
+    ws, res = base + (9 << 20), base + (10 << 20)
+
+    def call(i, o, sl, clip=0.0, wsb=ws_bytes):
+        args = abi.step_args(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                             max_grad_norm=clip, loss_scale=1.0, step=1)
+        with pytest.raises(abi.ZeroError) as e:
+            abi.zero_reduce_adam_step_1pass(plan, 0, rows, *i, *o, sl, ws, wsb, args, res, 0)
+        return e.value.code
+
+    assert call(ins, outs, slot, clip=1.0) == abi.ZERO_EINVAL
+    assert call(ins, [ins[0], outs[1], outs[2]], slot) == abi.ZERO_EINVAL       # out = in
+    assert call(ins, [outs[0], ins[2] + 4 * S - 16, outs[2]], slot) == abi.ZERO_EINVAL  # tail
+    assert call(ins, [outs[0], outs[0] + 16, outs[2]], slot) == abi.ZERO_EINVAL  # outs overlap
+    assert call(ins, outs, outs[2] + 4 * S - 2) == abi.ZERO_EINVAL              # slot overlaps v
+    assert call(ins, outs, ins[1] + 2) == abi.ZERO_EINVAL                       # slot in m_in
+    assert call(ins, [outs[0] + 4, outs[1], outs[2]], slot) == abi.ZERO_EALIGN
+    assert call(ins, outs, slot, wsb=16) == abi.ZERO_ENOSPC

@@ -100,7 +100,7 @@ MAX_SHARD_BF16 = dataclasses.replace(MAX_SHARD, name="max_shard_bf16", cfg_id=32
 
 
 def _cases():
-    return [pytest.param(w, r, id=f"{w.name}-r{r}") for w, r in (
+    cases = [pytest.param(w, r, False, id=f"{w.name}-r{r}") for w, r in (
         (synth.GPT2, 0), (synth.GPT2, 1), (synth.GPT2, 63),
         (synth.FLAT75, 0), (synth.FLAT75, 1),
         (synth.LLAMA3_8B, 0),
@@ -108,16 +108,19 @@ def _cases():
         (synth.LLAMA3_8B_BF16, 0), (synth.LLAMA3_8B_BF16, 7),
         (MAX_SHARD, 1), (MAX_SHARD_BF16, 1),
     )]
+    # the single-pass step (unclipped workloads) as bench.py --one-pass times it
+    cases += [pytest.param(synth.GPT2, r, True, id=f"gpt2_1p5b-r{r}-1pass") for r in (0, 1)]
+    return cases
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("w,rank", _cases())
-def test_full_size_shard(w, rank):
+@pytest.mark.parametrize("w,rank,one_pass", _cases())
+def test_full_size_shard(w, rank, one_pass):
     import zero_sharded_optimizer_rank_amd.abi as abi
     from zero_sharded_optimizer_rank_amd.shard import DeviceShard
 
-    print(f"[full size {w.name} rank {rank}]", flush=True)
-    dev = DeviceShard(w, rank)
+    print(f"[full size {w.name} rank {rank}{' one pass' if one_pass else ''}]", flush=True)
+    dev = DeviceShard(w, rank, one_pass=one_pass)
     dev.load_initial_state()
     p = orun.workload_plan(w)
     assert dev.count == p.shard and dev.flat_begin == rank * p.shard
@@ -135,8 +138,13 @@ def test_full_size_shard(w, rank):
         ovf_other = other_overflow_at(w, step, dev.flat_begin, dev.count)
         q_all, bad_all, cols = _feed_and_reduce(dev, step, scaler.scale, idx)
         args = dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq, other_overflow=ovf_other)
-        dev.step(args)
+        if one_pass:
+            dev.step_1pass(args)
+        else:
+            dev.step(args)
         res = dev.result()
+        if one_pass and not res.skip:
+            dev.adopt()
         sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, o_t + 1, w.world_size,
                                  o_scale)
         fin_fn = oracle.finalize_bf16 if bf16 else oracle.finalize
@@ -145,7 +153,9 @@ def test_full_size_shard(w, rank):
         check_result(res, fin, step)
         acc = (oracle.reduce_contributions_bf16 if bf16 else oracle.reduce_contributions)(cols)
         g = oracle.unscale(acc, sc.inv32)
-        assert np.array_equal(dev.fetch("grad", idx).view(np.uint32), g.view(np.uint32)), step
+        if not one_pass:  # the single pass writes no gradient
+            assert np.array_equal(dev.fetch("grad", idx).view(np.uint32),
+                                  g.view(np.uint32)), step
         if not fin.skip:
             op, om, ov, h = oracle.adam_apply(g, op, om, ov, sc, fin.coef)
             oh = oracle.f32_to_bf16(op) if bf16 else h.view(np.uint16)

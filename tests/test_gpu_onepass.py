@@ -1,0 +1,199 @@
+"""GPU parity of the single-pass step (zero_reduce_adam_step_1pass) for steps
+without clipping, through the C ABI against the CPU oracle.
+
+The single pass reduces, adds the exact squares and applies the update from
+the current master/m/v into a second set; the caller adopts that set only if
+the step was not skipped.  The bar is the two-pass step's: result word and
+every state element bit for bit; on a skipped step the current set must be
+exactly the state before the step.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import run as orun
+
+from parity_util import check_result, compare_state, run_window, StepReport
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _unclipped(w: synth.Workload) -> synth.Workload:
+    return dataclasses.replace(w, max_grad_norm=0.0)
+
+
+@pytest.mark.parametrize("variant", ["config", "skip"])
+def test_onepass_tiny_all_shards(variant):
+    """All four shards of the tiny workload.  Every rank runs its single pass
+    first; the exact all-reduce of the squared-norm integers and overflow flags
+    follows (zero_finalize with the other ranks' values), and each rank adopts
+    its new set only if no rank overflowed."""
+    import zero_sharded_optimizer_rank_amd.abi as abi
+    from zero_sharded_optimizer_rank_amd.shard import DeviceShard
+
+    w = synth.TINY
+    if variant == "skip":
+        w = dataclasses.replace(w, inject_step=2)
+    print(f"[onepass tiny_all_shards {variant}]", flush=True)
+    records = orun.run_all_ranks(w)
+    n = w.world_size
+    devs = [DeviceShard(w, r, one_pass=True) for r in range(n)]
+    for d in devs:
+        d.load_initial_state()
+    scaler = abi.new_scaler(w.loss_scale0)
+    skips = []
+    for rec in records:
+        assert rec.loss_scale == scaler.scale
+        for d in devs:
+            d.load_contributions(rec.step, scaler.scale)
+        base = devs[0].args(scaler.t + 1, scaler.scale)
+        for d in devs:
+            d.step_1pass(base)
+        rs = [d.result() for d in devs]
+        for r, d in enumerate(devs):
+            a = d.args(scaler.t + 1, scaler.scale,
+                       other_q=sum(rs[x].own_q for x in range(n) if x != r),
+                       other_overflow=any(rs[x].overflow for x in range(n) if x != r))
+            d.finalize(a)
+        skipped = None
+        for r, d in enumerate(devs):
+            res = d.result()
+            check_result(res, rec.fin[r], rec.step)
+            skipped = bool(res.skip)
+            if not skipped:
+                d.adopt()
+            rep = StepReport(rec.step, skipped, float(res.clip_coef))
+            st = rec.after[r]
+            for name, want in (("master", st.p), ("m", st.m), ("v", st.v),
+                               ("slot", st.h.view(np.uint16))):
+                compare_state(rep, name, d.fetch(name), want)
+            assert all(v == 0 for v in rep.mismatches.values()), (rec.step, r, rep.mismatches)
+            assert d.guards_intact()
+        skips.append(skipped)
+        abi.zero_scaler_update(scaler, skipped)
+        assert scaler.t == rec.t
+    assert skips == [s == w.inject_step for s in range(1, w.steps + 1)]
+    last = devs[-1]
+    for name in ("master", "m", "v", "slot"):
+        assert last.fetch(name)[-1] == 0  # the padding element stays exactly zero
+
+
+def _windows():
+    count = (1 << 20) + 3
+    cases = []
+    for w in (synth.GPT2, _unclipped(synth.FLAT75), _unclipped(synth.LLAMA3_8B)):
+        p = orun.workload_plan(w)
+        for r in w.parity_ranks:
+            if w.inject_step is not None and r == 0:
+                e = synth.inject_site(w, w.inject_step)[1]
+                begin = max(0, e - count // 2)
+            elif r == w.parity_ranks[-1]:
+                begin = p.shard - count
+            else:
+                begin = 12345
+            cases.append(pytest.param(w, r, begin, count, id=f"{w.name}-r{r}"))
+    return cases
+
+
+@pytest.mark.parametrize("w,rank,begin,count", _windows())
+def test_onepass_window_parity(w, rank, begin, count):
+    """Every step on a ~1M-element window of the parity ranks' shards: GPT-2
+    as configured (unclipped, dynamic loss scale), and the flat 7.5B and
+    Llama-3-8B workloads with clipping off (the latter skips its step 2, on
+    rank 0 from its own overflow and on the others from another rank's)."""
+    print(f"[onepass window {w.name} rank {rank} begin {begin} count {count}]", flush=True)
+    reps = run_window(w, rank, begin, count, one_pass=True)
+    if w.inject_step is not None:
+        assert reps[w.inject_step - 1].skip
+        assert not any(r.skip for i, r in enumerate(reps) if i != w.inject_step - 1)
+    assert all(r.coef == 1.0 for r in reps)
+
+
+@pytest.mark.parametrize("count", [1, 3, 4, 5, 255, 256, 257, 511, 4099])
+@pytest.mark.parametrize("begin", [0, 1, 2, 3, 5])
+def test_onepass_small_lengths_and_slot_offsets(begin, count):
+    """Shard lengths inside a quad, a wave and a workgroup, at every slot
+    alignment (flat offset mod 8), GPT-2 rank 1's geometry."""
+    w = synth.GPT2
+    print(f"[onepass small begin {begin} count {count}]", flush=True)
+    run_window(w, 1, begin, count, steps=2, one_pass=True)
+
+
+def test_onepass_empty_shard():
+    """S = 0: nothing to update; the result word is still written."""
+    import zero_sharded_optimizer_rank_amd.abi as abi
+    n = 4
+    plan = abi.zero_plan_t(0, n, 1, 0, 0)
+    ws = torch.zeros(abi.zero_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
+    res = torch.full((abi.RESULT_BYTES,), 0xFF, dtype=torch.uint8, device="cuda")
+    d = [torch.zeros(16, dtype=torch.float32, device="cuda") for _ in range(8)]
+    args = abi.step_args(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                         max_grad_norm=0.0, loss_scale=1.0, step=1)
+    abi.zero_reduce_adam_step_1pass(plan, 0, [d[0]] * n, *d[1:8], ws, ws.numel(), args, res)
+    torch.cuda.synchronize()
+    r = abi.zero_step_result_t.from_buffer_copy(res.cpu().numpy().tobytes())
+    assert r.own_q == 0 and r.norm == 0.0 and r.clip_coef == 1.0 and not r.skip
+    assert all(int(x.abs().sum().item()) == 0 for x in d)
+
+
+def test_onepass_matches_two_pass_bitwise():
+    """The single pass and the two-pass step leave the same bits (state, slot
+    and result word) on the same inputs."""
+    from zero_sharded_optimizer_rank_amd.shard import DeviceShard
+    w = synth.GPT2
+    print("[onepass vs two-pass]", flush=True)
+    a = DeviceShard(w, 63, 1000, 200_003, one_pass=True)
+    b = DeviceShard(w, 63, 1000, 200_003)
+    for d in (a, b):
+        d.load_initial_state()
+    for step in (1, 2, 3):
+        for d in (a, b):
+            d.load_contributions(step, w.loss_scale0)
+        args = a.args(step, w.loss_scale0, other_sq=0.5)
+        a.step_1pass(args)
+        b.step(args)
+        ra, rb = a.result(), b.result()
+        assert bytes(ra) == bytes(rb), step
+        assert not ra.skip
+        a.adopt()
+        for name in ("master", "m", "v", "slot"):
+            assert np.array_equal(a.fetch(name), b.fetch(name)), (step, name)
+
+
+def test_onepass_rejects_clipping_and_overlap():
+    import zero_sharded_optimizer_rank_amd.abi as abi
+    from zero_sharded_optimizer_rank_amd.shard import DeviceShard
+    w = synth.GPT2
+    d = DeviceShard(w, 0, 0, 4096, one_pass=True)
+    d.load_initial_state()
+    d.load_contributions(1, w.loss_scale0)
+    before = [d.fetch(x).copy() for x in ("master", "m", "v", "slot")]
+    with pytest.raises(abi.ZeroError) as e:
+        d.step_1pass(d.args(1, w.loss_scale0, max_norm=1.0))
+    assert e.value.code == abi.ZERO_EINVAL
+    ptrs = [d.contrib_ptrs(), d.master, d.m, d.v, d.master2, d.m2, d.v2,
+            d.slot_buf2.data_ptr() + 2 * d.slot_off]
+    for bad in ([d.master, d.m, d.v, d.master, d.m2, d.v2],      # out aliases in
+                [d.master, d.m, d.v, d.master2, d.master2, d.v2],  # outs alias
+                [d.master, d.m, d.v, d.master2, d.m2, d.m]):       # out aliases another in
+        with pytest.raises(abi.ZeroError) as e:
+            abi.zero_reduce_adam_step_1pass(d.plan, 0, ptrs[0], *bad, ptrs[7], d.ws,
+                                            d.ws.numel(), d.args(1, w.loss_scale0), d.res,
+                                            d.stream)
+        assert e.value.code == abi.ZERO_EINVAL
+    with pytest.raises(abi.ZeroError) as e:
+        abi.zero_reduce_adam_step_1pass(d.plan, 0, ptrs[0], *ptrs[1:7], ptrs[7], d.ws, 16,
+                                        d.args(1, w.loss_scale0), d.res, d.stream)
+    assert e.value.code == abi.ZERO_ENOSPC
+    after = [d.fetch(x) for x in ("master", "m", "v", "slot")]
+    assert all(np.array_equal(x, y) for x, y in zip(before, after))

@@ -115,6 +115,10 @@ _SIGNATURES = {
     "zero_reduce_adam_step": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _P(_vp), _vp, _vp,
                                              _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                              _P(zero_step_args_t), _vp, _vp]),
+    "zero_reduce_adam_step_1pass": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _P(_vp),
+                                                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                   ctypes.c_size_t, _P(zero_step_args_t), _vp,
+                                                   _vp]),
     "zero_reduce_check_bf16": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _P(_vp),
                                               _P(zero_step_args_t), _vp, _vp, ctypes.c_size_t,
                                               _vp, _vp]),
@@ -277,6 +281,17 @@ def zero_reduce_adam_step(plan, rank, contrib, master, m, v, param16_slot, grad_
                                        _addr(master), _addr(m), _addr(v), _addr(param16_slot),
                                        _addr(grad_out), _addr(workspace), ws_bytes,
                                        ctypes.byref(args), _addr(dev_result), _stream(stream)))
+
+
+def zero_reduce_adam_step_1pass(plan, rank, contrib, master_in, m_in, v_in, master_out, m_out,
+                                v_out, param16_slot_out, workspace, ws_bytes, args, dev_result,
+                                stream=None):
+    _check(lib().zero_reduce_adam_step_1pass(ctypes.byref(plan), rank, _ptr_array(contrib),
+                                             _addr(master_in), _addr(m_in), _addr(v_in),
+                                             _addr(master_out), _addr(m_out), _addr(v_out),
+                                             _addr(param16_slot_out), _addr(workspace), ws_bytes,
+                                             ctypes.byref(args), _addr(dev_result),
+                                             _stream(stream)))
 
 
 def zero_reduce_check_bf16(plan, rank, contrib, args, grad_out, workspace, ws_bytes, dev_result,

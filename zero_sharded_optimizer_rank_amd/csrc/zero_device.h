@@ -41,6 +41,12 @@
 #ifndef ZK_K2_NT_STORE
 #define ZK_K2_NT_STORE 1
 #endif
+#ifndef ZK_K12_NT_LOAD
+#define ZK_K12_NT_LOAD 1
+#endif
+#ifndef ZK_K12_NT_STORE
+#define ZK_K12_NT_STORE 1
+#endif
 // LDS the Adam kernels reserve and never touch, to cap how many of their
 // one-wave workgroups a CU holds: 160 KiB / 14848 B = 11.  With the default
 // 32 waves per CU the eight streams of the update thrash the memory system;
@@ -63,6 +69,19 @@
 #ifndef ZK_K1_LDS
 #define ZK_K1_LDS 13312
 #endif
+// The single-pass kernel (reduce and update in one pass, steps without
+// clipping) streams N + 3 inputs and 4 outputs and runs best at 8 of its
+// two-wave workgroups per CU at every N.  Measured on Llama-3-8B's shard
+// (N = 8) and the flat 7.5B shard (N = 64), clipping off, cap none / 16 /
+// 14 / 12 / 10 / 8 / 6 / 5 / 4 / 3 workgroups per CU: N = 8: 5.43 / 5.69 /
+// 5.56 / 5.94 / 6.01 / 6.13 / 6.03 / 4.86 / 4.06 / 2.98 TB/s; N = 64:
+// 5.47 / 5.51 / 5.51 / 5.68 / 5.81 / 5.80 / 5.48 / 4.53 / 3.76 / 2.72.
+#ifndef ZK_K12_LDS_SMALL_N
+#define ZK_K12_LDS_SMALL_N 20480
+#endif
+#ifndef ZK_K12_LDS
+#define ZK_K12_LDS 20480
+#endif
 // The bf16 reduce kernel (longer-lived waves: fp64 squares and a shuffle
 // tree per quad) runs best at 12 workgroups per CU for every N; at N = 8,
 // cap 8 / 10 / 11 / 12 / 13 / 14 / 16 / none: 5.31 / 6.06 / 6.35 / 6.61 /
@@ -76,6 +95,7 @@ namespace dev {
 
 // Reserved LDS of a reduce launch over n contribution rows.
 inline unsigned k1_lds(int n) { return n <= 8 ? ZK_K1_LDS_SMALL_N : ZK_K1_LDS; }
+inline unsigned k12_lds(int n) { return n <= 8 ? ZK_K12_LDS_SMALL_N : ZK_K12_LDS; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -256,15 +276,14 @@ __device__ inline void finalize_into(uint64_t qlo, uint64_t qhi, uint32_t bad,
 }
 
 // ---------------------------------------------------------------------------
-// Reduce side, per 4-element quad: load 8 bytes from each of the n rows, sum
-// in rank order from +0, write the quad of g (16 bytes), add the exact
-// squares.  Rows gives row(r), a pointer to rank r's fp16 values.
+// Reduce side, per 4-element quad: load 8 bytes from each of the n rows and
+// sum them in rank order from +0.  Rows gives row(r), a pointer to rank r's
+// fp16 values.
 template <typename Rows>
-__device__ __forceinline__ void reduce_quad(const Rows& rows, int32_t n, int64_t qd, float inv32,
-                                            float* __restrict__ grad, uint64_t& qlo,
-                                            uint64_t& qhi, uint32_t& bad) {
-  const int64_t off = qd * 4;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+__device__ __forceinline__ void sum_rows_quad(const Rows& rows, int32_t n, int64_t off,
+                                              float (&acc)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = 0.0f;
   for (int r0 = 0; r0 < n; r0 += kRankBatch) {
     u32x2 d[kRankBatch];
 #pragma unroll
@@ -281,6 +300,17 @@ __device__ __forceinline__ void reduce_quad(const Rows& rows, int32_t n, int64_t
       }
     }
   }
+}
+
+// The reduce kernel's quad: the row sum, the quad of g (16 bytes) and the
+// exact squares.
+template <typename Rows>
+__device__ __forceinline__ void reduce_quad(const Rows& rows, int32_t n, int64_t qd, float inv32,
+                                            float* __restrict__ grad, uint64_t& qlo,
+                                            uint64_t& qhi, uint32_t& bad) {
+  const int64_t off = qd * 4;
+  float acc[4];
+  sum_rows_quad(rows, n, off, acc);
   f32x4 g;
 #pragma unroll
   for (int e = 0; e < 4; ++e) g[e] = acc[e] * inv32;
@@ -343,20 +373,45 @@ __device__ __forceinline__ void adam1(float g, float c, const AdamScalars& sc, f
   p = p * sc.decay - u;
 }
 
+// The fp16 (or bf16) results of one wave-contiguous quad (element e in bits
+// 16e..16e+15 of h) go to slot[] with aligned 8-byte stores at any slot
+// alignment: when the slot is not 8-byte aligned, lane i writes the word
+// holding its last `me` results and lane i+1's first 4 - me (through a shuffle
+// every lane of the wave takes part in); the pieces at a wave's edges or the
+// segment's end go out as 2-byte stores.  Every lane of the wave must call
+// this; `valid` says whether the lane's quad is a whole quad of the segment.
+__device__ __forceinline__ void store_slot_quad(uint16_t* __restrict__ slot, uint64_t h,
+                                                bool valid, int64_t qd, int64_t full) {
+  const uint32_t me = (uint32_t)(((uintptr_t)slot >> 1) & 3u);
+  const uint32_t lane = threadIdx.x & 63u;
+  const int64_t off = qd * 4;
+  if (me == 0) {
+    if (valid) vstore<ZK_K2_NT_STORE>(h, (uint64_t*)(slot + off));
+  } else {
+    const uint64_t hn = shfl_down_u64(h, 1);
+    const bool right = lane < 63u && qd + 1 < full;
+    if (valid) {
+      if (lane == 0u) {
+        for (uint32_t e = 0; e < 4u - me; ++e) slot[off + e] = (uint16_t)(h >> (16 * e));
+      }
+      if (right) {
+        vstore<ZK_K2_NT_STORE>((h >> (16 * (4u - me))) | (hn << (16 * me)),
+                               (uint64_t*)(slot + off + 4 - me));
+      } else {
+        for (uint32_t e = 4u - me; e < 4u; ++e) slot[off + e] = (uint16_t)(h >> (16 * e));
+      }
+    }
+  }
+}
+
 // Adam body for one wave-contiguous quad of a segment: thread's quad qd of a
 // segment with `shard` elements (full = shard / 4 whole quads).  The quads of
-// a wave must be consecutive.  The fp16 results go to slot[] with aligned
-// 8-byte stores at any slot alignment: when the slot is not 8-byte aligned,
-// lane i writes the word holding its last `me` results and lane i+1's first
-// 4 - me (through a shuffle every lane of the wave takes part in); the pieces
-// at a wave's edges or the segment's end go out as 2-byte stores.
+// a wave must be consecutive.
 template <Fmt F = Fmt::F16>
 __device__ inline void adam_quad(const float* __restrict__ grad, float* __restrict__ master,
                                  float* __restrict__ mom, float* __restrict__ var,
                                  uint16_t* __restrict__ slot, int64_t shard, int64_t qd, float c,
                                  const AdamScalars& sc) {
-  const uint32_t me = (uint32_t)(((uintptr_t)slot >> 1) & 3u);
-  const uint32_t lane = threadIdx.x & 63u;
   const int64_t full = shard >> 2;
   const bool valid = qd < full;
   const int64_t off = qd * 4;
@@ -379,23 +434,7 @@ __device__ inline void adam_quad(const float* __restrict__ grad, float* __restri
     vstore<ZK_K2_NT_STORE>(m, (f32x4*)(mom + off));
     vstore<ZK_K2_NT_STORE>(v, (f32x4*)(var + off));
   }
-  if (me == 0) {
-    if (valid) vstore<ZK_K2_NT_STORE>(h, (uint64_t*)(slot + off));
-  } else {
-    const uint64_t hn = shfl_down_u64(h, 1);
-    const bool right = lane < 63u && qd + 1 < full;
-    if (valid) {
-      if (lane == 0u) {
-        for (uint32_t e = 0; e < 4u - me; ++e) slot[off + e] = (uint16_t)(h >> (16 * e));
-      }
-      if (right) {
-        vstore<ZK_K2_NT_STORE>((h >> (16 * (4u - me))) | (hn << (16 * me)),
-                               (uint64_t*)(slot + off + 4 - me));
-      } else {
-        for (uint32_t e = 4u - me; e < 4u; ++e) slot[off + e] = (uint16_t)(h >> (16 * e));
-      }
-    }
-  }
+  store_slot_quad(slot, h, valid, qd, full);
   if (qd == full) {
     // the ragged tail: the last shard % 4 elements, one by one
     for (int64_t j = full * 4; j < shard; ++j) {
@@ -405,6 +444,71 @@ __device__ inline void adam_quad(const float* __restrict__ grad, float* __restri
       mom[j] = mm;
       var[j] = vv;
       slot[j] = (uint16_t)from_f32<F>(pp);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Single pass for a step without clipping: the update needs no global value
+// but the skip decision, so one pass can reduce a quad, add its exact squares
+// and apply Adam (clip coefficient 1) from the `in` state to a second,
+// distinct `out` state and slot.  The partial goes out as in the reduce
+// kernel; the caller adopts `out` only if the finalized step is not skipped,
+// so `in` survives a skip untouched.  No gradient is written.
+struct StatePair {
+  const float* __restrict__ p_in;
+  const float* __restrict__ m_in;
+  const float* __restrict__ v_in;
+  float* __restrict__ p_out;
+  float* __restrict__ m_out;
+  float* __restrict__ v_out;
+  uint16_t* __restrict__ slot_out;
+};
+
+template <typename Rows>
+__device__ inline void reduce_adam_quad(const Rows& rows, int32_t n, int64_t shard, int64_t qd,
+                                        float inv32, const StatePair& st, const AdamScalars& sc,
+                                        uint64_t& qlo, uint64_t& qhi, uint32_t& bad) {
+  const int64_t full = shard >> 2;
+  const bool valid = qd < full;
+  const int64_t off = qd * 4;
+  uint64_t h = 0;
+  if (valid) {
+    f32x4 p = vload<ZK_K12_NT_LOAD>((const f32x4*)(st.p_in + off));
+    f32x4 m = vload<ZK_K12_NT_LOAD>((const f32x4*)(st.m_in + off));
+    f32x4 v = vload<ZK_K12_NT_LOAD>((const f32x4*)(st.v_in + off));
+    float acc[4];
+    sum_rows_quad(rows, n, off, acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint64_t lo, hi;
+      sq_units(acc[e], lo, hi, bad);
+      add128(qlo, qhi, lo, hi);
+      float pp = p[e], mm = m[e], vv = v[e];
+      adam1(acc[e] * inv32, 1.0f, sc, pp, mm, vv);
+      p[e] = pp;
+      m[e] = mm;
+      v[e] = vv;
+      h |= (uint64_t)f2h(pp) << (16 * e);
+    }
+    vstore<ZK_K12_NT_STORE>(p, (f32x4*)(st.p_out + off));
+    vstore<ZK_K12_NT_STORE>(m, (f32x4*)(st.m_out + off));
+    vstore<ZK_K12_NT_STORE>(v, (f32x4*)(st.v_out + off));
+  }
+  store_slot_quad(st.slot_out, h, valid, qd, full);
+  if (qd == full) {
+    for (int64_t j = full * 4; j < shard; ++j) {
+      float a = 0.0f;
+      for (int r = 0; r < n; ++r) a = a + h2f(rows.row(r)[j]);
+      uint64_t lo, hi;
+      sq_units(a, lo, hi, bad);
+      add128(qlo, qhi, lo, hi);
+      float pp = st.p_in[j], mm = st.m_in[j], vv = st.v_in[j];
+      adam1(a * inv32, 1.0f, sc, pp, mm, vv);
+      st.p_out[j] = pp;
+      st.m_out[j] = mm;
+      st.v_out[j] = vv;
+      st.slot_out[j] = (uint16_t)f2h(pp);
     }
   }
 }

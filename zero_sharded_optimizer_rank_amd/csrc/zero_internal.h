@@ -50,6 +50,16 @@ int launch_adam(const float* grad, float* master, float* m, float* v, uint16_t* 
                 hipStream_t stream);
 void* workspace_partials(void* workspace);
 
+// Single pass for steps without clipping: reduce, exact squares and the
+// update from the `in` state into the distinct `out` state and slot, then the
+// partial sums and finalize.  No gradient is written.
+int64_t k12_blocks(int64_t shard);
+int launch_reduce_adam_1pass(const uint16_t* const* contrib, int n, int64_t shard, float inv32,
+                             const float* master_in, const float* m_in, const float* v_in,
+                             float* master_out, float* m_out, float* v_out, uint16_t* slot_out,
+                             const AdamScalars& sc, void* workspace, const FinalizeArgs& fa,
+                             zero_step_result_t* res, hipStream_t stream);
+
 // bf16 path (the norm is a fixed pairwise fp64 tree; see zero_device.h).
 int64_t k1_blocks_bf16(int64_t shard);
 int launch_reduce_check_bf16(const uint16_t* const* contrib, int n, int64_t shard, float inv32,

@@ -69,6 +69,21 @@ __global__ __launch_bounds__(ZK_K2_THREADS) void k2_adam(
   }
 }
 
+// K12 (single pass, steps without clipping): K1's reduce and partial plus
+// the update with clip coefficient 1, from the `in` state into the distinct
+// `out` state and slot.  KF then finalizes as after K1.
+__global__ __launch_bounds__(ZK_K1_THREADS) void k12_reduce_adam(
+    ContribTable ct, int32_t n, int64_t shard, float inv32, StatePair st, AdamScalars sc,
+    Partial* __restrict__ partials, uint32_t* __restrict__ ticket) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
+  uint64_t qlo = 0, qhi = 0;
+  uint32_t bad = 0;
+  const int64_t qd = (int64_t)blockIdx.x * ZK_K1_THREADS + threadIdx.x;
+  reduce_adam_quad(ct, n, shard, qd, inv32, st, sc, qlo, qhi, bad);
+  block_reduce<ZK_K1_THREADS>(qlo, qhi, bad);
+  if (threadIdx.x == 0) partials[blockIdx.x] = make_partial(qlo, qhi, bad);
+}
+
 // --- bf16 path -------------------------------------------------------------
 __global__ __launch_bounds__(ZK_K1_THREADS) void k1_reduce_check_bf16(
     ContribTable ct, int32_t n, int64_t shard, float inv32, float* __restrict__ grad,
@@ -133,6 +148,8 @@ int64_t k1_blocks(int64_t shard) {
   return b < 1 ? 1 : b;
 }
 
+int64_t k12_blocks(int64_t shard) { return k1_blocks_bf16(shard); }  // one quad per thread
+
 int64_t k2_blocks(int64_t shard) {
   const int64_t quads = (shard + 3) >> 2;
   const int64_t per = (int64_t)ZK_K2_THREADS * ZK_K2_QUADS;
@@ -145,8 +162,11 @@ size_t workspace_bytes_for_blocks(int64_t reduce_blocks) {
 }
 
 size_t workspace_bytes(int64_t shard) {
-  const int64_t a = k1_blocks(shard), b = k1_blocks_bf16(shard);
-  return workspace_bytes_for_blocks(a > b ? a : b);
+  int64_t a = k1_blocks(shard);
+  const int64_t b = k1_blocks_bf16(shard), c = k12_blocks(shard);
+  if (b > a) a = b;
+  if (c > a) a = c;
+  return workspace_bytes_for_blocks(a);
 }
 
 void* workspace_partials(void* workspace) {
@@ -192,6 +212,23 @@ int launch_finalize_empty(const FinalizeArgs& fa, zero_step_result_t* res, hipSt
 int launch_finalize(const FinalizeArgs& fa, zero_step_result_t* res, hipStream_t stream) {
   hipLaunchKernelGGL(k_finalize, dim3(1), dim3(64), 0, stream, fa, res);
   return (int)hipGetLastError();
+}
+
+int launch_reduce_adam_1pass(const uint16_t* const* contrib, int n, int64_t shard, float inv32,
+                             const float* master_in, const float* m_in, const float* v_in,
+                             float* master_out, float* m_out, float* v_out, uint16_t* slot_out,
+                             const AdamScalars& sc, void* workspace, const FinalizeArgs& fa,
+                             zero_step_result_t* res, hipStream_t stream) {
+  ContribTable ct;
+  for (int r = 0; r < ZERO_MAX_RANKS; ++r) ct.p[r] = r < n ? contrib[r] : nullptr;
+  const StatePair st{master_in, m_in, v_in, master_out, m_out, v_out, slot_out};
+  const int64_t blocks = k12_blocks(shard);
+  hipLaunchKernelGGL(k12_reduce_adam, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), k12_lds(n),
+                     stream, ct, n, shard, inv32, st, sc,
+                     (Partial*)workspace_partials(workspace), (uint32_t*)workspace);
+  const int e = (int)hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_partials_finalize(workspace, blocks, fa, res, stream);
 }
 
 int launch_reduce_check_bf16(const uint16_t* const* contrib, int n, int64_t shard, float inv32,

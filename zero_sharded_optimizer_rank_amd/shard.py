@@ -38,7 +38,7 @@ def round_up(x: int, a: int) -> int:
 class DeviceShard:
     def __init__(self, w: synth.Workload, rank: int, begin: int = 0, count: Optional[int] = None,
                  device: str = "cuda:0", stream: Optional[torch.cuda.Stream] = None,
-                 row_align: int = ROW_ALIGN, device_state: bool = True):
+                 row_align: int = ROW_ALIGN, device_state: bool = True, one_pass: bool = False):
         self.w = w
         self.rank = rank
         self.device = torch.device(device)
@@ -67,11 +67,16 @@ class DeviceShard:
         e = max(count, 1)
         self.row_pitch = round_up(2 * ld, STAGGER_PERIOD) + STAGGER
         st_pitch = round_up(4 * e, STAGGER_PERIOD) + STAGGER
-        n_state = 4 if device_state else 1
+        # one_pass: a second master/m/v set and slot for zero_reduce_adam_step_1pass,
+        # which writes the other set and leaves the current one as it was
+        self.one_pass = one_pass and device_state
+        n_state = (7 if self.one_pass else 4) if device_state else 1
         rows_end = round_up(n * self.row_pitch, STAGGER_PERIOD)
         slot_elems = GUARD + 8 + count + GUARD
         slot_at = round_up(rows_end + n_state * st_pitch, STAGGER_PERIOD) + STAGGER
-        self.arena = torch.empty(slot_at + 2 * slot_elems, dtype=torch.uint8, device=self.device)
+        slot2_at = slot_at + round_up(2 * slot_elems, STAGGER_PERIOD) + STAGGER
+        end = (slot2_at if self.one_pass else slot_at) + 2 * slot_elems
+        self.arena = torch.empty(end, dtype=torch.uint8, device=self.device)
         a16 = self.arena.view(torch.int16)
         self.contrib = a16.as_strided((n, ld), (self.row_pitch // 2, 1), 0)
 
@@ -85,11 +90,18 @@ class DeviceShard:
             self.v.zero_()
         else:
             self.master = self.m = self.v = None
+        if self.one_pass:
+            self.master2, self.m2, self.v2 = state(4), state(5), state(6)
         # slot with the real buffer's alignment (flat_begin mod 8) plus guards
         self.mis = self.flat_begin % 8
         self.slot_buf = self.arena[slot_at:slot_at + 2 * slot_elems].view(torch.int16)
         self.slot_buf.fill_(GUARD_WORD)
         self.slot_off = GUARD + self.mis
+        self.slot_buf2 = None
+        if self.one_pass:
+            # same alignment as the first slot: both buffers start on 4 KiB boundaries
+            self.slot_buf2 = self.arena[slot2_at:slot2_at + 2 * slot_elems].view(torch.int16)
+            self.slot_buf2.fill_(GUARD_WORD)
         self.ws = torch.zeros(abi.zero_workspace_bytes(self.plan), dtype=torch.uint8,
                               device=self.device)
         self.res = torch.zeros(abi.RESULT_BYTES, dtype=torch.uint8, device=self.device)
@@ -112,10 +124,14 @@ class DeviceShard:
         return [base + self.row_pitch * r for r in range(self.w.world_size)]
 
     def guards_intact(self) -> bool:
-        b = self.slot_buf
-        lo = b[:self.slot_off]
-        hi = b[self.slot_off + self.count:]
-        return bool((lo == GUARD_WORD).all().item()) and bool((hi == GUARD_WORD).all().item())
+        for b in (self.slot_buf, self.slot_buf2):
+            if b is None:
+                continue
+            lo = b[:self.slot_off]
+            hi = b[self.slot_off + self.count:]
+            if not ((lo == GUARD_WORD).all().item() and (hi == GUARD_WORD).all().item()):
+                return False
+        return True
 
     # ---------------------------------------------------------------- feeding
     def _feed16(self, row: torch.Tensor, fill):
@@ -181,6 +197,24 @@ class DeviceShard:
         f(self.plan, self.rank_in_plan, self.contrib_ptrs(), self.master,
                                   self.m, self.v, self.slot_ptr(), self.grad, self.ws,
                                   self.ws.numel(), args, self.res, self.stream)
+
+    def step_1pass(self, args, res: Optional[torch.Tensor] = None):
+        """zero_reduce_adam_step_1pass from the current master/m/v and slot into
+        the other set; adopt() makes that set current once the step is known
+        not to have been skipped."""
+        if not self.one_pass:
+            raise RuntimeError("this shard was built without the second state set")
+        abi.zero_reduce_adam_step_1pass(
+            self.plan, self.rank_in_plan, self.contrib_ptrs(), self.master, self.m, self.v,
+            self.master2, self.m2, self.v2, self.slot_buf2.data_ptr() + 2 * self.slot_off,
+            self.ws, self.ws.numel(), args, self.res if res is None else res, self.stream)
+
+    def adopt(self):
+        """Make the set the last step_1pass wrote the current one."""
+        self.master, self.master2 = self.master2, self.master
+        self.m, self.m2 = self.m2, self.m
+        self.v, self.v2 = self.v2, self.v
+        self.slot_buf, self.slot_buf2 = self.slot_buf2, self.slot_buf
 
     @property
     def rank_in_plan(self) -> int:
