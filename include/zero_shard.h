@@ -168,8 +168,9 @@ typedef struct zero_step_result {
   int32_t reserved;
 } zero_step_result_t;
 
-/* Bytes of workspace zero_reduce_check needs for plan->shard elements:
- * 256 + 16 * (256 + ceil(ceil(S / 4) / 128)), about S / 32 bytes; 0 for a
+/* Bytes of workspace the reduce (zero_reduce_check and the other calls that
+ * take a workspace) needs for plan->shard elements:
+ * 256 + 16 * (256 + ceil(ceil(S / 4) / 64)), about S / 16 bytes; 0 for a
  * NULL plan or a shard outside 0..ZERO_MAX_SHARD.  The workspace needs no
  * initialisation (the reduce kernel arms its own counter). */
 size_t zero_workspace_bytes(const zero_plan_t* plan);

@@ -102,8 +102,8 @@ def test_host_argument_errors():
     assert abi.zero_plan_real(plan, 5) == -1
     for shard in (0, 1, 8, 2048, 2049, 10**9):
         p = abi.zero_plan_t(shard, 1, 1, shard, shard)
-        quads = -(-shard // 4)  # one reduce workgroup per 128 quads
-        assert abi.zero_workspace_bytes(p) == 256 + 16 * (256 + max(1, -(-quads // 128)))
+        quads = -(-shard // 4)  # one single-pass workgroup per 64 quads (the most partials)
+        assert abi.zero_workspace_bytes(p) == 256 + 16 * (256 + max(1, -(-quads // 64)))
     assert abi.zero_workspace_bytes(abi.zero_plan_t(0, 1, 1, -1, -1)) == 0
     assert abi.RESULT_BYTES == 56
 

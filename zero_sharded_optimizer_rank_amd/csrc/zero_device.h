@@ -41,6 +41,12 @@
 #ifndef ZK_K2_NT_STORE
 #define ZK_K2_NT_STORE 1
 #endif
+#ifndef ZK_K12_THREADS
+#define ZK_K12_THREADS 64  // threads per single-pass workgroup (a multiple of 64)
+#endif
+#ifndef ZK_K12_BATCH
+#define ZK_K12_BATCH 4  // contribution rows the single pass loads before summing
+#endif
 #ifndef ZK_K12_NT_LOAD
 #define ZK_K12_NT_LOAD 1
 #endif
@@ -70,17 +76,20 @@
 #define ZK_K1_LDS 13312
 #endif
 // The single-pass kernel (reduce and update in one pass, steps without
-// clipping) streams N + 3 inputs and 4 outputs and runs best at 8 of its
-// two-wave workgroups per CU at every N.  Measured on Llama-3-8B's shard
-// (N = 8) and the flat 7.5B shard (N = 64), clipping off, cap none / 16 /
-// 14 / 12 / 10 / 8 / 6 / 5 / 4 / 3 workgroups per CU: N = 8: 5.43 / 5.69 /
-// 5.56 / 5.94 / 6.01 / 6.13 / 6.03 / 4.86 / 4.06 / 2.98 TB/s; N = 64:
-// 5.47 / 5.51 / 5.51 / 5.68 / 5.81 / 5.80 / 5.48 / 4.53 / 3.76 / 2.72.
+// clipping) streams N + 3 inputs and 4 outputs.  One-wave workgroups, 16 per
+// CU for N <= 8 and 20 beyond (10240 and 8192 B of reserved LDS).  Measured
+// (step ms, clipping off; Llama-3-8B N = 8 / GPT-2 N = 64 / flat 7.5B
+// N = 64): one wave, cap 16: 6.73 / 0.657 / 3.14; cap 20: 6.81 / 0.651 /
+// 3.15; cap 24: 6.95 / 0.658 / 3.21; two waves, cap 8: 6.88 / 0.677 / 3.11;
+// four waves, cap 5: 6.98 / 0.669 / 3.11; two waves with 2 or 8 rows per
+// load batch: 6.80-7.20 / 0.68-0.81 / 3.15-3.77.  Two-wave caps from none to
+// 3 per CU at N = 8 ran at 5.43 (none) to 6.13 TB/s (8 per CU), then fell
+// to 2.98 at 3 per CU.
 #ifndef ZK_K12_LDS_SMALL_N
-#define ZK_K12_LDS_SMALL_N 20480
+#define ZK_K12_LDS_SMALL_N 10240
 #endif
 #ifndef ZK_K12_LDS
-#define ZK_K12_LDS 20480
+#define ZK_K12_LDS 8192
 #endif
 // The bf16 reduce kernel (longer-lived waves: fp64 squares and a shuffle
 // tree per quad) runs best at 12 workgroups per CU for every N; at N = 8,
@@ -279,18 +288,18 @@ __device__ inline void finalize_into(uint64_t qlo, uint64_t qhi, uint32_t bad,
 // Reduce side, per 4-element quad: load 8 bytes from each of the n rows and
 // sum them in rank order from +0.  Rows gives row(r), a pointer to rank r's
 // fp16 values.
-template <typename Rows>
+template <int B = kRankBatch, typename Rows>
 __device__ __forceinline__ void sum_rows_quad(const Rows& rows, int32_t n, int64_t off,
                                               float (&acc)[4]) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) acc[e] = 0.0f;
-  for (int r0 = 0; r0 < n; r0 += kRankBatch) {
-    u32x2 d[kRankBatch];
+  for (int r0 = 0; r0 < n; r0 += B) {
+    u32x2 d[B];
 #pragma unroll
-    for (int b = 0; b < kRankBatch; ++b)
+    for (int b = 0; b < B; ++b)
       if (r0 + b < n) d[b] = vload<ZK_K1_NT_LOAD>((const u32x2*)(rows.row(r0 + b) + off));
 #pragma unroll
-    for (int b = 0; b < kRankBatch; ++b) {
+    for (int b = 0; b < B; ++b) {
       if (r0 + b < n) {
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
@@ -478,7 +487,7 @@ __device__ inline void reduce_adam_quad(const Rows& rows, int32_t n, int64_t sha
     f32x4 m = vload<ZK_K12_NT_LOAD>((const f32x4*)(st.m_in + off));
     f32x4 v = vload<ZK_K12_NT_LOAD>((const f32x4*)(st.v_in + off));
     float acc[4];
-    sum_rows_quad(rows, n, off, acc);
+    sum_rows_quad<ZK_K12_BATCH>(rows, n, off, acc);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       uint64_t lo, hi;

@@ -72,15 +72,15 @@ __global__ __launch_bounds__(ZK_K2_THREADS) void k2_adam(
 // K12 (single pass, steps without clipping): K1's reduce and partial plus
 // the update with clip coefficient 1, from the `in` state into the distinct
 // `out` state and slot.  KF then finalizes as after K1.
-__global__ __launch_bounds__(ZK_K1_THREADS) void k12_reduce_adam(
+__global__ __launch_bounds__(ZK_K12_THREADS) void k12_reduce_adam(
     ContribTable ct, int32_t n, int64_t shard, float inv32, StatePair st, AdamScalars sc,
     Partial* __restrict__ partials, uint32_t* __restrict__ ticket) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
   uint64_t qlo = 0, qhi = 0;
   uint32_t bad = 0;
-  const int64_t qd = (int64_t)blockIdx.x * ZK_K1_THREADS + threadIdx.x;
+  const int64_t qd = (int64_t)blockIdx.x * ZK_K12_THREADS + threadIdx.x;
   reduce_adam_quad(ct, n, shard, qd, inv32, st, sc, qlo, qhi, bad);
-  block_reduce<ZK_K1_THREADS>(qlo, qhi, bad);
+  block_reduce<ZK_K12_THREADS>(qlo, qhi, bad);
   if (threadIdx.x == 0) partials[blockIdx.x] = make_partial(qlo, qhi, bad);
 }
 
@@ -148,7 +148,11 @@ int64_t k1_blocks(int64_t shard) {
   return b < 1 ? 1 : b;
 }
 
-int64_t k12_blocks(int64_t shard) { return k1_blocks_bf16(shard); }  // one quad per thread
+int64_t k12_blocks(int64_t shard) {  // one quad per thread
+  const int64_t quads = (shard + 3) >> 2;
+  const int64_t b = (quads + ZK_K12_THREADS - 1) / ZK_K12_THREADS;
+  return b < 1 ? 1 : b;
+}
 
 int64_t k2_blocks(int64_t shard) {
   const int64_t quads = (shard + 3) >> 2;
@@ -223,7 +227,7 @@ int launch_reduce_adam_1pass(const uint16_t* const* contrib, int n, int64_t shar
   for (int r = 0; r < ZERO_MAX_RANKS; ++r) ct.p[r] = r < n ? contrib[r] : nullptr;
   const StatePair st{master_in, m_in, v_in, master_out, m_out, v_out, slot_out};
   const int64_t blocks = k12_blocks(shard);
-  hipLaunchKernelGGL(k12_reduce_adam, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), k12_lds(n),
+  hipLaunchKernelGGL(k12_reduce_adam, dim3((uint32_t)blocks), dim3(ZK_K12_THREADS), k12_lds(n),
                      stream, ct, n, shard, inv32, st, sc,
                      (Partial*)workspace_partials(workspace), (uint32_t*)workspace);
   const int e = (int)hipGetLastError();
