@@ -16,7 +16,8 @@ Prints one JSON line.  Fields beyond the common ones:
   roofline      the dominant kernel's algorithmic bytes per launch over its
                 average HIP-event duration, against the 8 TB/s HBM peak
   kernels       the same figures for both kernels
-  cpu_baseline  the CPU oracle timed on a bounded window of the same shard
+  cpu_baseline  the CPU oracle timed on bounded windows of the same shard, in
+                one process and in one process per host core (at most 16)
 """
 from __future__ import annotations
 
@@ -66,33 +67,94 @@ def traffic_for(workload: str, kernel: str):
     return None if k is None else k.get("bytes_per_launch")
 
 
-def cpu_baseline(w, seconds: float):
-    """The oracle as it is, on rank 0's first 2^25 shard elements, repeated
-    for about `seconds`; input generation is outside the timing."""
+def _oracle_inputs(w, begin: int, n: int):
     import oracle
     from oracle import run as orun
 
     p = orun.workload_plan(w)
-    n = min(1 << 25, p.shard)
-    c = orun.shard_contrib(w, p, 0, 1, w.loss_scale0, 0, n)
-    pm, m, v, h = orun.initial_state(w, p, 0, 0, n)
+    c = orun.shard_contrib(w, p, 0, 1, w.loss_scale0, begin, n)
+    pm, m, v, h = orun.initial_state(w, p, 0, begin, n)
     other_sq = w.other_sq(p.real(0)) if w.other_ranks_from_config else 0.0
+    return c, pm, m, v, h, other_sq
+
+
+def _oracle_steps(w, inputs, reps: int = 0, seconds: float = 0.0):
+    """Run the oracle's whole step on one window again and again, carrying the
+    state: `reps` times, or until `seconds` have passed (at least twice).
+    Returns (steps, elapsed seconds)."""
+    import oracle
+
+    c, pm, m, v, h, other_sq = inputs
     step_fn = oracle.shard_step_bf16 if w.dtype == "bf16" else oracle.shard_step
-    reps, t0 = 0, time.perf_counter()
-    t_applied = 0
+    done, t_applied, t0 = 0, 0, time.perf_counter()
     while True:
         sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, t_applied + 1,
                                  w.world_size, w.loss_scale0)
         out = step_fn(c, pm, m, v, h, sc, w.max_grad_norm, other_sq=other_sq)
         pm, m, v, h = out.p, out.m, out.v, out.h
         t_applied += 0 if out.fin.skip else 1
-        reps += 1
+        done += 1
         el = time.perf_counter() - t0
-        if reps >= 2 and el >= seconds:
-            break
-    return {"value": n * reps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"{w.name} rank 0 shard elements [0, {n}) x {w.world_size} contributions, "
-                      f"{reps} oracle steps (numpy, one thread), {el:.1f} s"}
+        if (reps and done >= reps) or (not reps and done >= 2 and el >= seconds):
+            return done, el
+
+
+_BARRIER = None
+
+
+def _pool_init(barrier):
+    global _BARRIER
+    _BARRIER = barrier
+
+
+def _oracle_worker(args):
+    """One process of the parallel baseline: its own window of the shard,
+    generated before the common start, then `reps` oracle steps."""
+    w, begin, n, reps = args
+    inputs = _oracle_inputs(w, begin, n)
+    _BARRIER.wait()
+    t0 = time.time()
+    done, _ = _oracle_steps(w, inputs, reps=reps)
+    return n * done, t0, time.time()
+
+
+def cpu_baseline(w, seconds: float, procs: int):
+    """The oracle as it is, on rank 0's shard, timed on the host's cores:
+    first one process on the first 2^25 elements for about `seconds`, then
+    `procs` processes at once, each on its own 2^23-element window, for about
+    as long.  Input generation is outside the timing.  The workers are fresh
+    interpreters (spawned: the seeded generator's OpenMP runtime does not
+    survive a fork), started before anything touches the GPU."""
+    import multiprocessing as mp
+
+    from oracle import run as orun
+
+    shard = orun.workload_plan(w).shard
+    n1 = min(1 << 25, shard)
+    steps1, el1 = _oracle_steps(w, _oracle_inputs(w, 0, n1), seconds=seconds)
+    rate1 = n1 * steps1 / el1
+    out = {"unit": "params/s", "kind": "oracle",
+           "single_process": {"value": rate1, "cores": 1,
+                              "sample": f"{w.name} rank 0 shard elements [0, {n1}) x "
+                                        f"{w.world_size} contributions, {steps1} oracle steps "
+                                        f"(numpy, one process), {el1:.1f} s"}}
+    nw = min(1 << 23, max(1, shard // max(procs, 1)))
+    procs = min(procs, max(1, shard // nw))
+    if procs <= 1:
+        out.update(value=rate1, cores=1, sample=out["single_process"]["sample"])
+        return out
+    reps = max(2, int(seconds * rate1 / nw))
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(procs)
+    with ctx.Pool(procs, initializer=_pool_init, initargs=(barrier,)) as pool:
+        res = pool.map(_oracle_worker, [(w, k * nw, nw, reps) for k in range(procs)])
+    total = sum(r[0] for r in res)
+    wall = max(r[2] for r in res) - min(r[1] for r in res)
+    out.update(value=total / wall, cores=procs,
+               sample=f"{w.name} rank 0 shard, {procs} processes each on its own {nw}-element "
+                      f"window x {w.world_size} contributions, {reps} oracle steps each "
+                      f"(numpy, one thread per process), {wall:.1f} s wall")
+    return out
 
 
 def calibration_copy(nbytes: float, stream):
@@ -136,6 +198,9 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-procs", type=int, default=0,
+                    help="processes of the parallel CPU oracle baseline (0: the CPUs this "
+                         "process may use, at most 16)")
     ap.add_argument("--row-align", type=int, default=None,
                     help="contribution row stride alignment in elements (default: the runtime's)")
     ap.add_argument("--time-skip", action="store_true",
@@ -163,17 +228,25 @@ def main():
               "(the multi-GPU exchange around the step is not built)", file=sys.stderr)
         sys.exit(2)
 
-    import torch
-
     import synth
-    from zero_sharded_optimizer_rank_amd import abi
-    from zero_sharded_optimizer_rank_amd.shard import DeviceShard
 
-    abi.lib()
     w = synth.BY_NAME[a.workload]
     if a.no_clip:
         import dataclasses
         w = dataclasses.replace(w, max_grad_norm=0.0)
+    # the CPU baseline starts worker processes: it runs before anything
+    # touches the GPU
+    cpu = None
+    if (not a.no_cpu_baseline and w.units is None and not a.offload and not a.one_pass):
+        cpu = cpu_baseline(w, a.cpu_seconds, a.cpu_procs or
+                           max(1, min(16, len(os.sched_getaffinity(0)))))
+
+    import torch
+
+    from zero_sharded_optimizer_rank_amd import abi
+    from zero_sharded_optimizer_rank_amd.shard import DeviceShard
+
+    abi.lib()
     if a.offload:
         return offload_main(a, w)
     if a.one_pass:
@@ -292,8 +365,8 @@ def main():
         "setup_s": setup_s,
         "kernel_hash": kernel_hash(),
     }
-    if not a.no_cpu_baseline and w.units is None:
-        out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 
