@@ -200,7 +200,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-procs", type=int, default=0,
                     help="processes of the parallel CPU oracle baseline (0: the CPUs this "
-                         "process may use, at most 16)")
+                         "process may use, at most 16; 1 under a GPU profiler, whose preloaded "
+                         "library the worker processes would inherit)")
     ap.add_argument("--row-align", type=int, default=None,
                     help="contribution row stride alignment in elements (default: the runtime's)")
     ap.add_argument("--time-skip", action="store_true",
