@@ -377,10 +377,11 @@ def one_pass_main(a, w):
     from zero_sharded_optimizer_rank_amd import abi
     from zero_sharded_optimizer_rank_amd.shard import DeviceShard
 
-    if w.max_grad_norm > 0 or w.dtype != "fp16" or w.units is not None:
-        print("--one-pass takes a flat fp16 workload without clipping (add --no-clip to turn "
+    if w.max_grad_norm > 0 or w.units is not None:
+        print("--one-pass takes a flat workload without clipping (add --no-clip to turn "
               "a workload's clipping off)", file=sys.stderr)
         sys.exit(2)
+    kname = "k12_reduce_adam_bf16" if w.dtype == "bf16" else "k12_reduce_adam"
     dev = DeviceShard(w, a.rank, one_pass=True)
     real = abi.zero_plan_real(dev.full_plan, a.rank)
     S, n, stream = dev.count, w.world_size, dev.stream
@@ -424,16 +425,16 @@ def one_pass_main(a, w):
         "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{w.name}: rank {a.rank} of N={n}, shard S={S} (psi={w.psi}), "
-                               f"fp16 contributions and slot, fp32 master/m/v in two sets, "
+                               f"{w.dtype} contributions and slot, fp32 master/m/v in two sets, "
                                f"single-pass step"
                                + (" (clipping turned off)" if a.no_clip else " (no clipping)"),
                    "world_size_simulated": n, "shard": S, "psi": w.psi},
         "step_ms_p10_p50_p90": [per_step[int(q * (len(per_step) - 1))] for q in (0.1, 0.5, 0.9)],
         "hbm_gbps_step": bpp * S / (ms * 1e6),
-        "roofline": {"bound": "hbm", "kernel": "k12_reduce_adam", "achieved": gbps,
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic_for(w.name + "_1pass", "k12_reduce_adam")},
-        "kernels": {"k12_reduce_adam": {"ms": k_ms, "bytes_per_param": bpp, "bytes": bpp * S,
+                     "traffic": traffic_for(w.name + "_1pass", kname)},
+        "kernels": {kname: {"ms": k_ms, "bytes_per_param": bpp, "bytes": bpp * S,
                                         "gbps": gbps,
                                         "note": "event pair spans the pass and the finalize"}},
         "calibration_copy": calib,

@@ -308,6 +308,17 @@ int zero_reduce_adam_step_bf16(const zero_plan_t* plan, int32_t rank,
                                uint16_t* param_bf16_slot, float* grad_out, void* workspace,
                                size_t ws_bytes, const zero_step_args_t* args,
                                zero_step_result_t* dev_result, hipStream_t stream);
+/* zero_reduce_adam_step_1pass_bf16: zero_reduce_adam_step_1pass with bf16
+ * contribution rows and a bf16 slot, and dev_result as zero_reduce_check_bf16
+ * writes it (the pairwise tree norm; args->other_q must be 0).  Arguments,
+ * results and errors otherwise as zero_reduce_adam_step_1pass. */
+int zero_reduce_adam_step_1pass_bf16(const zero_plan_t* plan, int32_t rank,
+                                     const uint16_t* const* contrib, const float* master_in,
+                                     const float* m_in, const float* v_in, float* master_out,
+                                     float* m_out, float* v_out, uint16_t* param_bf16_slot_out,
+                                     void* workspace, size_t ws_bytes,
+                                     const zero_step_args_t* args,
+                                     zero_step_result_t* dev_result, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* ZeRO-Offload form of the update ("10.6 ZeRO 与 FSDP" §10.6.6: the GPU

@@ -91,7 +91,8 @@ def test_onepass_tiny_all_shards(variant):
 def _windows():
     count = (1 << 20) + 3
     cases = []
-    for w in (synth.GPT2, _unclipped(synth.FLAT75), _unclipped(synth.LLAMA3_8B)):
+    for w in (synth.GPT2, _unclipped(synth.FLAT75), _unclipped(synth.LLAMA3_8B),
+              _unclipped(synth.LLAMA3_8B_BF16)):
         p = orun.workload_plan(w)
         for r in w.parity_ranks:
             if w.inject_step is not None and r == 0:
@@ -129,6 +130,68 @@ def test_onepass_small_lengths_and_slot_offsets(begin, count):
     run_window(w, 1, begin, count, steps=2, one_pass=True)
 
 
+@pytest.mark.parametrize("count", [1, 5, 511, 513, 512 * 256 + 1, 512 * 512 + 3])
+@pytest.mark.parametrize("begin", [0, 3])
+def test_onepass_bf16_lengths_and_tree_chunks(begin, count):
+    """bf16: lengths inside a quad and a workgroup, and around the tree
+    kernel's chunk transitions, at two slot alignments."""
+    w = _unclipped(synth.LLAMA3_8B_BF16)
+    print(f"[onepass bf16 begin {begin} count {count}]", flush=True)
+    run_window(w, 1, 4096 + begin, count, steps=2, one_pass=True)
+
+
+@pytest.mark.parametrize("variant", ["config", "skip"])
+def test_onepass_bf16_tiny_all_shards(variant):
+    """bf16, all four tiny shards: each rank's pass first, then the other
+    ranks' squared norms (summed in rank order) and overflow flags through
+    zero_finalize_bf16, and the adoption only if no rank overflowed."""
+    import zero_sharded_optimizer_rank_amd.abi as abi
+    from zero_sharded_optimizer_rank_amd.shard import DeviceShard
+    from test_gpu_bf16 import _oracle_all_ranks
+
+    w = synth.TINY_BF16
+    if variant == "skip":
+        w = dataclasses.replace(w, inject_step=2)
+    print(f"[onepass bf16 tiny_all_shards {variant}]", flush=True)
+    records = _oracle_all_ranks(w, w.max_grad_norm, w.steps)
+    n = w.world_size
+    devs = [DeviceShard(w, r, one_pass=True) for r in range(n)]
+    for d in devs:
+        d.load_initial_state()
+    scaler = abi.new_scaler(w.loss_scale0)
+    for step, scale, fins, _gs, states, t in records:
+        assert scale == scaler.scale
+        for d in devs:
+            d.load_contributions(step, scaler.scale)
+        base = devs[0].args(scaler.t + 1, scaler.scale)
+        for d in devs:
+            d.step_1pass(base)
+        rs = [d.result() for d in devs]
+        for r, d in enumerate(devs):
+            other = 0.0
+            for x in range(n):
+                if x != r:
+                    other += rs[x].own_sq
+            d.finalize(d.args(scaler.t + 1, scaler.scale, other_sq=other,
+                              other_overflow=any(rs[x].overflow for x in range(n) if x != r)))
+        skipped = None
+        for r, d in enumerate(devs):
+            res = d.result()
+            check_result(res, fins[r], step)
+            skipped = bool(res.skip)
+            if not skipped:
+                d.adopt()
+            rep = StepReport(step, skipped, float(res.clip_coef))
+            for name, want in zip(("master", "m", "v", "slot"), states[r]):
+                compare_state(rep, name, d.fetch(name), want)
+            assert all(v == 0 for v in rep.mismatches.values()), (step, r, rep.mismatches)
+            assert d.guards_intact()
+        if variant == "skip":
+            assert skipped == (step == 2)
+        abi.zero_scaler_update(scaler, skipped)
+        assert scaler.t == t
+
+
 def test_onepass_empty_shard():
     """S = 0: nothing to update; the result word is still written."""
     import zero_sharded_optimizer_rank_amd.abi as abi
@@ -146,20 +209,22 @@ def test_onepass_empty_shard():
     assert all(int(x.abs().sum().item()) == 0 for x in d)
 
 
-def test_onepass_matches_two_pass_bitwise():
+@pytest.mark.parametrize("wname", ["gpt2_1p5b", "llama3_8b_bf16"])
+def test_onepass_matches_two_pass_bitwise(wname):
     """The single pass and the two-pass step leave the same bits (state, slot
     and result word) on the same inputs."""
     from zero_sharded_optimizer_rank_amd.shard import DeviceShard
-    w = synth.GPT2
-    print("[onepass vs two-pass]", flush=True)
-    a = DeviceShard(w, 63, 1000, 200_003, one_pass=True)
-    b = DeviceShard(w, 63, 1000, 200_003)
+    w = _unclipped(synth.BY_NAME[wname])
+    print(f"[onepass vs two-pass {wname}]", flush=True)
+    rank = w.world_size - 1
+    a = DeviceShard(w, rank, 1000, 200_003, one_pass=True)
+    b = DeviceShard(w, rank, 1000, 200_003)
     for d in (a, b):
         d.load_initial_state()
     for step in (1, 2, 3):
         for d in (a, b):
             d.load_contributions(step, w.loss_scale0)
-        args = a.args(step, w.loss_scale0, other_sq=0.5)
+        args = a.args(step, w.loss_scale0, max_norm=0.0, other_sq=0.5)
         a.step_1pass(args)
         b.step(args)
         ra, rb = a.result(), b.result()

@@ -149,12 +149,10 @@ def test_random_configuration_offload_matches_oracle(seed):
 
 @pytest.mark.parametrize("seed", range(16))
 def test_random_configuration_onepass_matches_oracle(seed):
-    """The single-pass step on random fp16 configurations with clipping off,
-    whole shards or windows, injected overflow included."""
+    """The single-pass step on random fp16 and bf16 configurations with
+    clipping off, whole shards or windows, injected overflow included."""
     w = random_workload(200 + seed)
     w = dataclasses.replace(w, max_grad_norm=0.0)
-    if w.dtype != "fp16":
-        w = dataclasses.replace(w, dtype="fp16", loss_scale0=1024.0)
     p = orun.workload_plan(w)
     rng = np.random.default_rng([0x7A41, seed])
     for rank in w.parity_ranks:
@@ -163,7 +161,7 @@ def test_random_configuration_onepass_matches_oracle(seed):
             count = int(rng.integers(1, p.shard - begin + 1))
         else:
             begin, count = 0, p.shard
-        print(f"[random onepass {seed}] N={w.world_size} psi={w.psi} S={p.shard} rank={rank} "
+        print(f"[random onepass {seed}] {w.dtype} N={w.world_size} psi={w.psi} S={p.shard} rank={rank} "
               f"window=({begin},{count}) scale={w.loss_scale0} sigma={w.sigma} "
               f"inject={w.inject_step}", flush=True)
         run_window(w, rank, begin, count, one_pass=True)

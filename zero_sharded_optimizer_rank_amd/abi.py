@@ -119,6 +119,10 @@ _SIGNATURES = {
                                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                    ctypes.c_size_t, _P(zero_step_args_t), _vp,
                                                    _vp]),
+    "zero_reduce_adam_step_1pass_bf16": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32,
+                                                        _P(_vp), _vp, _vp, _vp, _vp, _vp, _vp,
+                                                        _vp, _vp, ctypes.c_size_t,
+                                                        _P(zero_step_args_t), _vp, _vp]),
     "zero_reduce_check_bf16": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _P(_vp),
                                               _P(zero_step_args_t), _vp, _vp, ctypes.c_size_t,
                                               _vp, _vp]),
@@ -292,6 +296,18 @@ def zero_reduce_adam_step_1pass(plan, rank, contrib, master_in, m_in, v_in, mast
                                              _addr(param16_slot_out), _addr(workspace), ws_bytes,
                                              ctypes.byref(args), _addr(dev_result),
                                              _stream(stream)))
+
+
+def zero_reduce_adam_step_1pass_bf16(plan, rank, contrib, master_in, m_in, v_in, master_out,
+                                     m_out, v_out, param_bf16_slot_out, workspace, ws_bytes, args,
+                                     dev_result, stream=None):
+    _check(lib().zero_reduce_adam_step_1pass_bf16(ctypes.byref(plan), rank, _ptr_array(contrib),
+                                                  _addr(master_in), _addr(m_in), _addr(v_in),
+                                                  _addr(master_out), _addr(m_out),
+                                                  _addr(v_out), _addr(param_bf16_slot_out),
+                                                  _addr(workspace), ws_bytes,
+                                                  ctypes.byref(args), _addr(dev_result),
+                                                  _stream(stream)))
 
 
 def zero_reduce_check_bf16(plan, rank, contrib, args, grad_out, workspace, ws_bytes, dev_result,

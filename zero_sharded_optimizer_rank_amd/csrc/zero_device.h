@@ -91,6 +91,12 @@
 #ifndef ZK_K12_LDS
 #define ZK_K12_LDS 8192
 #endif
+// The bf16 single pass keeps two-wave workgroups (one tree partial per 512
+// elements, so the largest shard stays within the tree kernel's chunk) and
+// the two-wave single pass's best cap, 8 per CU.
+#ifndef ZK_K12B_LDS
+#define ZK_K12B_LDS 20480
+#endif
 // The bf16 reduce kernel (longer-lived waves: fp64 squares and a shuffle
 // tree per quad) runs best at 12 workgroups per CU for every N; at N = 8,
 // cap 8 / 10 / 11 / 12 / 13 / 14 / 16 / none: 5.31 / 6.06 / 6.35 / 6.61 /
@@ -665,6 +671,72 @@ __device__ inline Partial reduce_block_bf16(const Rows& rows, int32_t n, int64_t
   double x = reduce_quad_bf16(rows, n, q_first + threadIdx.x, shard, inv32, grad, bad);
   block_tree<ZK_K1_THREADS>(x, bad);
   return Partial{(uint64_t)__double_as_longlong(x), (uint64_t)(bad ? 1u : 0u) << 63};
+}
+
+// Single pass, bf16: the quad's row sum, its tree node (as reduce_quad_bf16)
+// and the update with coefficient 1 from the `in` state into the `out`
+// state and bf16 slot.  Returns the quad's node; elements past the shard
+// count +0.
+template <typename Rows>
+__device__ inline double reduce_adam_quad_bf16(const Rows& rows, int32_t n, int64_t shard,
+                                               int64_t qd, float inv32, const StatePair& st,
+                                               const AdamScalars& sc, uint32_t& bad) {
+  const int64_t full = shard >> 2;
+  const bool valid = qd < full;
+  const int64_t off = qd * 4;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  uint64_t h = 0;
+  if (valid) {
+    f32x4 p = vload<ZK_K12_NT_LOAD>((const f32x4*)(st.p_in + off));
+    f32x4 m = vload<ZK_K12_NT_LOAD>((const f32x4*)(st.m_in + off));
+    f32x4 v = vload<ZK_K12_NT_LOAD>((const f32x4*)(st.v_in + off));
+    for (int r0 = 0; r0 < n; r0 += kRankBatch) {
+      u32x2 d[kRankBatch];
+#pragma unroll
+      for (int b = 0; b < kRankBatch; ++b)
+        if (r0 + b < n) d[b] = vload<ZK_K1_NT_LOAD>((const u32x2*)(rows.row(r0 + b) + off));
+#pragma unroll
+      for (int b = 0; b < kRankBatch; ++b) {
+        if (r0 + b < n) {
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            acc[2 * w] = acc[2 * w] + bf2f(d[b][w] & 0xFFFFu);
+            acc[2 * w + 1] = acc[2 * w + 1] + bf2f(d[b][w] >> 16);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float pp = p[e], mm = m[e], vv = v[e];
+      adam1(acc[e] * inv32, 1.0f, sc, pp, mm, vv);
+      p[e] = pp;
+      m[e] = mm;
+      v[e] = vv;
+      h |= (uint64_t)f2bf(pp) << (16 * e);
+    }
+    vstore<ZK_K12_NT_STORE>(p, (f32x4*)(st.p_out + off));
+    vstore<ZK_K12_NT_STORE>(m, (f32x4*)(st.m_out + off));
+    vstore<ZK_K12_NT_STORE>(v, (f32x4*)(st.v_out + off));
+  }
+  store_slot_quad(st.slot_out, h, valid, qd, full);
+  if (qd == full) {
+    for (int64_t j = off; j < shard; ++j) {
+      float a = 0.0f;
+      for (int r = 0; r < n; ++r) a = a + bf2f(rows.row(r)[j]);
+      acc[j - off] = a;
+      float pp = st.p_in[j], mm = st.m_in[j], vv = st.v_in[j];
+      adam1(a * inv32, 1.0f, sc, pp, mm, vv);
+      st.p_out[j] = pp;
+      st.m_out[j] = mm;
+      st.v_out[j] = vv;
+      st.slot_out[j] = (uint16_t)f2bf(pp);
+    }
+  } else if (!valid) {
+    return 0.0;
+  }
+  return (sq_or_zero(acc[0], bad) + sq_or_zero(acc[1], bad)) +
+         (sq_or_zero(acc[2], bad) + sq_or_zero(acc[3], bad));
 }
 
 __device__ inline void finalize_bf16_into(double tree, uint32_t bad, const FinalizeArgs& fa,

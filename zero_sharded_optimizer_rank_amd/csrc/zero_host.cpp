@@ -298,6 +298,45 @@ static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Checks of the single-pass calls: no clipping, reduce inputs, state
+// pointers, and no out buffer overlapping an in buffer or another out buffer.
+static int check_1pass(const zero_plan_t* plan, int32_t rank, const uint16_t* const* contrib,
+                       const float* master_in, const float* m_in, const float* v_in,
+                       float* master_out, float* m_out, float* v_out,
+                       uint16_t* param16_slot_out, void* workspace, size_t ws_bytes,
+                       const zero_step_args_t* args, zero_step_result_t* dev_result) {
+  int rc = check_plan_rank(plan, rank);
+  if (!rc) rc = check_adam_args(args);
+  if (rc) return rc;
+  if (args->max_grad_norm > 0.0)
+    return fail(ZERO_EINVAL,
+                "max_grad_norm > 0: clipping needs the whole norm before any update "
+                "(use the two-pass step)");
+  rc = check_reduce_inputs(plan, contrib, workspace, ws_bytes, dev_result);
+  if (rc) return rc;
+  const int64_t S = plan->shard;
+  if (S == 0) return ZERO_OK;
+  if (!master_in || !m_in || !v_in || !master_out || !m_out || !v_out || !param16_slot_out)
+    return fail(ZERO_EINVAL, "NULL state pointer");
+  if (!aligned(master_in, 16) || !aligned(m_in, 16) || !aligned(v_in, 16) ||
+      !aligned(master_out, 16) || !aligned(m_out, 16) || !aligned(v_out, 16))
+    return fail(ZERO_EALIGN, "master, m and v (in and out) must be 16-byte aligned");
+  if (!aligned(param16_slot_out, 2)) return fail(ZERO_EALIGN, "slot_out not 2-byte aligned");
+  const size_t b4 = 4 * (size_t)S, b2 = 2 * (size_t)S;
+  const void* ins[3] = {master_in, m_in, v_in};
+  const void* outs[4] = {master_out, m_out, v_out, param16_slot_out};
+  const size_t out_bytes[4] = {b4, b4, b4, b2};
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 3; ++i)
+      if (overlap(outs[o], out_bytes[o], ins[i], b4))
+        return fail(ZERO_EINVAL, "an output state buffer overlaps an input state buffer");
+    for (int q = 0; q < o; ++q)
+      if (overlap(outs[o], out_bytes[o], outs[q], out_bytes[q]))
+        return fail(ZERO_EINVAL, "output state buffers overlap");
+  }
+  return ZERO_OK;
+}
+
 int zero_reduce_adam_step_1pass(const zero_plan_t* plan, int32_t rank,
                                 const uint16_t* const* contrib, const float* master_in,
                                 const float* m_in, const float* v_in, float* master_out,
@@ -305,44 +344,37 @@ int zero_reduce_adam_step_1pass(const zero_plan_t* plan, int32_t rank,
                                 void* workspace, size_t ws_bytes, const zero_step_args_t* args,
                                 zero_step_result_t* dev_result, hipStream_t stream) {
   g_err[0] = 0;
-  int rc = check_plan_rank(plan, rank);
-  if (!rc) rc = check_adam_args(args);
+  const int rc = check_1pass(plan, rank, contrib, master_in, m_in, v_in, master_out, m_out,
+                             v_out, param16_slot_out, workspace, ws_bytes, args, dev_result);
   if (rc) return rc;
-  if (args->max_grad_norm > 0.0)
-    return fail(ZERO_EINVAL,
-                "max_grad_norm > 0: clipping needs the whole norm before any update "
-                "(use zero_reduce_adam_step)");
-  rc = check_reduce_inputs(plan, contrib, workspace, ws_bytes, dev_result);
-  if (rc) return rc;
-  const int64_t S = plan->shard;
-  if (S > 0) {
-    if (!master_in || !m_in || !v_in || !master_out || !m_out || !v_out || !param16_slot_out)
-      return fail(ZERO_EINVAL, "NULL state pointer");
-    if (!aligned(master_in, 16) || !aligned(m_in, 16) || !aligned(v_in, 16) ||
-        !aligned(master_out, 16) || !aligned(m_out, 16) || !aligned(v_out, 16))
-      return fail(ZERO_EALIGN, "master, m and v (in and out) must be 16-byte aligned");
-    if (!aligned(param16_slot_out, 2))
-      return fail(ZERO_EALIGN, "param16_slot_out not 2-byte aligned");
-    const size_t b4 = 4 * (size_t)S, b2 = 2 * (size_t)S;
-    const void* ins[3] = {master_in, m_in, v_in};
-    const void* outs[4] = {master_out, m_out, v_out, param16_slot_out};
-    const size_t out_bytes[4] = {b4, b4, b4, b2};
-    for (int o = 0; o < 4; ++o) {
-      for (int i = 0; i < 3; ++i)
-        if (overlap(outs[o], out_bytes[o], ins[i], b4))
-          return fail(ZERO_EINVAL, "an output state buffer overlaps an input state buffer");
-      for (int p = 0; p < o; ++p)
-        if (overlap(outs[o], out_bytes[o], outs[p], out_bytes[p]))
-          return fail(ZERO_EINVAL, "output state buffers overlap");
-    }
-  }
   const zk::FinalizeArgs fa = finalize_args(plan, args);
-  return hip_status(zk::launch_reduce_adam_1pass(contrib, (int)plan->world_size, S,
+  return hip_status(zk::launch_reduce_adam_1pass(contrib, (int)plan->world_size, plan->shard,
                                                  (float)fa.inv64, master_in, m_in, v_in,
                                                  master_out, m_out, v_out, param16_slot_out,
                                                  adam_scalars(args), workspace, fa, dev_result,
                                                  stream),
                     "reduce_adam_1pass launch");
+}
+
+int zero_reduce_adam_step_1pass_bf16(const zero_plan_t* plan, int32_t rank,
+                                     const uint16_t* const* contrib, const float* master_in,
+                                     const float* m_in, const float* v_in, float* master_out,
+                                     float* m_out, float* v_out, uint16_t* param_bf16_slot_out,
+                                     void* workspace, size_t ws_bytes,
+                                     const zero_step_args_t* args,
+                                     zero_step_result_t* dev_result, hipStream_t stream) {
+  g_err[0] = 0;
+  int rc = check_1pass(plan, rank, contrib, master_in, m_in, v_in, master_out, m_out, v_out,
+                       param_bf16_slot_out, workspace, ws_bytes, args, dev_result);
+  if (!rc && (args->other_q_lo || args->other_q_hi))
+    rc = fail(ZERO_EINVAL, "the bf16 path takes the other ranks' share as other_sq only");
+  if (rc) return rc;
+  const zk::FinalizeArgs fa = finalize_args(plan, args);
+  return hip_status(zk::launch_reduce_adam_1pass_bf16(
+                        contrib, (int)plan->world_size, plan->shard, (float)fa.inv64, master_in,
+                        m_in, v_in, master_out, m_out, v_out, param_bf16_slot_out,
+                        adam_scalars(args), workspace, fa, dev_result, stream),
+                    "reduce_adam_1pass_bf16 launch");
 }
 
 int zero_reduce_check_bf16(const zero_plan_t* plan, int32_t rank, const uint16_t* const* contrib,

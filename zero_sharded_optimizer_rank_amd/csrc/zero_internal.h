@@ -66,6 +66,12 @@ int launch_reduce_check_bf16(const uint16_t* const* contrib, int n, int64_t shar
                              float* grad, void* workspace, const FinalizeArgs& fa,
                              zero_step_result_t* res, hipStream_t stream);
 int launch_finalize_bf16(const FinalizeArgs& fa, zero_step_result_t* res, hipStream_t stream);
+int launch_reduce_adam_1pass_bf16(const uint16_t* const* contrib, int n, int64_t shard,
+                                  float inv32, const float* master_in, const float* m_in,
+                                  const float* v_in, float* master_out, float* m_out,
+                                  float* v_out, uint16_t* slot_out, const AdamScalars& sc,
+                                  void* workspace, const FinalizeArgs& fa,
+                                  zero_step_result_t* res, hipStream_t stream);
 int launch_adam_bf16(const float* grad, float* master, float* m, float* v, uint16_t* slot,
                      int64_t shard, const AdamScalars& sc, const zero_step_result_t* res,
                      hipStream_t stream);

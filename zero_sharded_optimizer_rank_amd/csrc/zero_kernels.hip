@@ -94,6 +94,19 @@ __global__ __launch_bounds__(ZK_K1_THREADS) void k1_reduce_check_bf16(
   if (threadIdx.x == 0) partials[blockIdx.x] = pt;
 }
 
+// K12 in bf16: the single pass with the bf16 tree partial of K1's bf16 form.
+__global__ __launch_bounds__(ZK_K1_THREADS) void k12_reduce_adam_bf16(
+    ContribTable ct, int32_t n, int64_t shard, float inv32, StatePair st, AdamScalars sc,
+    Partial* __restrict__ partials, uint32_t* __restrict__ ticket) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
+  uint32_t bad = 0;
+  const int64_t qd = (int64_t)blockIdx.x * ZK_K1_THREADS + threadIdx.x;
+  double x = reduce_adam_quad_bf16(ct, n, shard, qd, inv32, st, sc, bad);
+  block_tree<ZK_K1_THREADS>(x, bad);
+  if (threadIdx.x == 0)
+    partials[blockIdx.x] = Partial{(uint64_t)__double_as_longlong(x), (uint64_t)(bad ? 1u : 0u) << 63};
+}
+
 __global__ __launch_bounds__(kThreads) void kt_tree_finalize_bf16(
     const Partial* __restrict__ partials, int64_t n_partials, int chunk,
     Partial* __restrict__ level2, uint32_t* __restrict__ ticket, FinalizeArgs fa,
@@ -235,20 +248,13 @@ int launch_reduce_adam_1pass(const uint16_t* const* contrib, int n, int64_t shar
   return launch_partials_finalize(workspace, blocks, fa, res, stream);
 }
 
-int launch_reduce_check_bf16(const uint16_t* const* contrib, int n, int64_t shard, float inv32,
-                             float* grad, void* workspace, const FinalizeArgs& fa,
-                             zero_step_result_t* res, hipStream_t stream) {
-  ContribTable ct;
-  for (int r = 0; r < ZERO_MAX_RANKS; ++r) ct.p[r] = r < n ? contrib[r] : nullptr;
-  const int64_t blocks = k1_blocks_bf16(shard);
+// The bf16 tree kernel over `blocks` workgroup partials: power-of-two chunks
+// with at most kFinBlocks workgroups, the last one finalizing.
+static int launch_tree_finalize_bf16(void* workspace, int64_t blocks, const FinalizeArgs& fa,
+                                     zero_step_result_t* res, hipStream_t stream) {
   uint32_t* ticket = (uint32_t*)workspace;
   Partial* level2 = (Partial*)((char*)workspace + kTicketBytes);
   Partial* partials = (Partial*)workspace_partials(workspace);
-  hipLaunchKernelGGL(k1_reduce_check_bf16, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), ZK_K1B_LDS, stream,
-                     ct, n, shard, inv32, grad, partials, ticket);
-  int e = (int)hipGetLastError();
-  if (e != hipSuccess) return e;
-  // chunk: a power of two with at most kFinBlocks workgroups over all partials
   int64_t per = (blocks + kFinBlocks - 1) / kFinBlocks;
   int64_t chunk = 1;
   while (chunk < per) chunk <<= 1;
@@ -257,6 +263,39 @@ int launch_reduce_check_bf16(const uint16_t* const* contrib, int n, int64_t shar
   hipLaunchKernelGGL(kt_tree_finalize_bf16, dim3((uint32_t)fb), dim3(kThreads), 0, stream,
                      partials, blocks, (int)chunk, level2, ticket, fa, res);
   return (int)hipGetLastError();
+}
+
+int launch_reduce_check_bf16(const uint16_t* const* contrib, int n, int64_t shard, float inv32,
+                             float* grad, void* workspace, const FinalizeArgs& fa,
+                             zero_step_result_t* res, hipStream_t stream) {
+  ContribTable ct;
+  for (int r = 0; r < ZERO_MAX_RANKS; ++r) ct.p[r] = r < n ? contrib[r] : nullptr;
+  const int64_t blocks = k1_blocks_bf16(shard);
+  uint32_t* ticket = (uint32_t*)workspace;
+  Partial* partials = (Partial*)workspace_partials(workspace);
+  hipLaunchKernelGGL(k1_reduce_check_bf16, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), ZK_K1B_LDS, stream,
+                     ct, n, shard, inv32, grad, partials, ticket);
+  int e = (int)hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_tree_finalize_bf16(workspace, blocks, fa, res, stream);
+}
+
+int launch_reduce_adam_1pass_bf16(const uint16_t* const* contrib, int n, int64_t shard,
+                                  float inv32, const float* master_in, const float* m_in,
+                                  const float* v_in, float* master_out, float* m_out,
+                                  float* v_out, uint16_t* slot_out, const AdamScalars& sc,
+                                  void* workspace, const FinalizeArgs& fa,
+                                  zero_step_result_t* res, hipStream_t stream) {
+  ContribTable ct;
+  for (int r = 0; r < ZERO_MAX_RANKS; ++r) ct.p[r] = r < n ? contrib[r] : nullptr;
+  const StatePair st{master_in, m_in, v_in, master_out, m_out, v_out, slot_out};
+  const int64_t blocks = k1_blocks_bf16(shard);
+  hipLaunchKernelGGL(k12_reduce_adam_bf16, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS),
+                     ZK_K12B_LDS, stream, ct, n, shard, inv32, st, sc,
+                     (Partial*)workspace_partials(workspace), (uint32_t*)workspace);
+  const int e = (int)hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_tree_finalize_bf16(workspace, blocks, fa, res, stream);
 }
 
 int launch_finalize_bf16(const FinalizeArgs& fa, zero_step_result_t* res, hipStream_t stream) {

@@ -204,13 +204,16 @@ class DeviceShard:
         not to have been skipped."""
         if not self.one_pass:
             raise RuntimeError("this shard was built without the second state set")
-        abi.zero_reduce_adam_step_1pass(
+        f = abi.zero_reduce_adam_step_1pass_bf16 if self.bf16 else abi.zero_reduce_adam_step_1pass
+        f(
             self.plan, self.rank_in_plan, self.contrib_ptrs(), self.master, self.m, self.v,
             self.master2, self.m2, self.v2, self.slot_buf2.data_ptr() + 2 * self.slot_off,
             self.ws, self.ws.numel(), args, self.res if res is None else res, self.stream)
 
     def adopt(self):
         """Make the set the last step_1pass wrote the current one."""
+        if not self.one_pass:
+            raise RuntimeError("this shard was built without the second state set")
         self.master, self.master2 = self.master2, self.master
         self.m, self.m2 = self.m2, self.m
         self.v, self.v2 = self.v2, self.v
