@@ -246,8 +246,8 @@ int zero_reduce_adam_step(const zero_plan_t* plan, int32_t rank, const uint16_t*
 
 /*
  * zero_reduce_adam_step_1pass: the whole step in one streaming pass, for steps
- * without gradient clipping (args->max_grad_norm <= 0), such as the GPT-2 and
- * small workloads whose configurations clip nothing.  Pages: as
+ * without gradient clipping (args->max_grad_norm <= 0), e.g. a GPT-2-sized
+ * model trained with dynamic loss scaling and no clipping.  Pages: as
  * zero_reduce_check and zero_adam_apply; the tutorial's loss scaling (§4.3)
  * supplies the only global dependency left, the skip on overflow.
  * Without clipping, no element's update depends on the shard's norm, only on
@@ -268,7 +268,9 @@ int zero_reduce_adam_step(const zero_plan_t* plan, int32_t rank, const uint16_t*
  * caller adopts them, e.g. by swapping buffer sets); when it is 1 they hold
  * unspecified values and the in state is the unchanged state (the caller
  * keeps it and its slot).  dev_result is bit-identical to zero_reduce_check's
- * with clip_coef 1.
+ * with clip_coef 1.  Across ranks, the caller all-reduces own_q and overflow
+ * after the pass and calls zero_finalize with the other ranks' values; the
+ * skip it writes then decides the adoption on every rank alike.
  * Errors: as zero_reduce_adam_step, plus ZERO_EINVAL for max_grad_norm > 0,
  * for an out buffer that overlaps an in buffer, and for out buffers that
  * overlap one another.  Nothing is launched if a check fails.
