@@ -377,14 +377,20 @@ def one_pass_main(a, w):
     from zero_sharded_optimizer_rank_amd import abi
     from zero_sharded_optimizer_rank_amd.shard import DeviceShard
 
-    if w.max_grad_norm > 0 or w.units is not None:
-        print("--one-pass takes a flat workload without clipping (add --no-clip to turn "
+    if w.max_grad_norm > 0:
+        print("--one-pass takes a workload without clipping (add --no-clip to turn "
               "a workload's clipping off)", file=sys.stderr)
         sys.exit(2)
-    kname = "k12_reduce_adam_bf16" if w.dtype == "bf16" else "k12_reduce_adam"
-    dev = DeviceShard(w, a.rank, one_pass=True)
-    real = abi.zero_plan_real(dev.full_plan, a.rank)
-    S, n, stream = dev.count, w.world_size, dev.stream
+    if w.units is not None:
+        from zero_sharded_optimizer_rank_amd.units import DeviceUnits
+        kname = "k12u_reduce_adam"
+        dev = DeviceUnits(w, a.rank, one_pass=True)
+        real, S = dev.real_count(), dev.plan.rank_shard
+    else:
+        kname = "k12_reduce_adam_bf16" if w.dtype == "bf16" else "k12_reduce_adam"
+        dev = DeviceShard(w, a.rank, one_pass=True)
+        real, S = abi.zero_plan_real(dev.full_plan, a.rank), dev.count
+    n, stream = w.world_size, dev.stream
     other_sq = w.other_sq(real) if w.other_ranks_from_config else 0.0
     t_setup = time.perf_counter()
     dev.load_initial_state()
@@ -415,6 +421,7 @@ def one_pass_main(a, w):
     ms = wall * 1e3 / a.steps
     k_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / a.steps
     per_step = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    n_units = getattr(dev, "n_units", None)
     del dev
     calib = calibration_copy(a.calib_bytes, stream)
     bpp = 2 * n + 26
@@ -427,6 +434,7 @@ def one_pass_main(a, w):
         "config": {"workload": f"{w.name}: rank {a.rank} of N={n}, shard S={S} (psi={w.psi}), "
                                f"{w.dtype} contributions and slot, fp32 master/m/v in two sets, "
                                f"single-pass step"
+                               + (f", {n_units} FSDP units" if w.units else "")
                                + (" (clipping turned off)" if a.no_clip else " (no clipping)"),
                    "world_size_simulated": n, "shard": S, "psi": w.psi},
         "step_ms_p10_p50_p90": [per_step[int(q * (len(per_step) - 1))] for q in (0.1, 0.5, 0.9)],

@@ -484,6 +484,35 @@ int zero_units_step(int32_t world_size, const zero_unit_buffers_t* units_host,
                     const zero_step_args_t* args, void* workspace, size_t ws_bytes,
                     zero_step_result_t* dev_result, hipStream_t stream);
 
+/*
+ * zero_units_step_1pass: zero_reduce_adam_step_1pass over all units at once,
+ * for steps without clipping (args->max_grad_norm <= 0).  One launch reduces
+ * every unit's rows, adds the exact squares and applies the update from each
+ * unit's current master, m, v (units_*) into the master, m, v and param16 of
+ * a second prepared table (out_*) with the same shards; no gradient is
+ * written.  dev_result is written as zero_units_reduce_check writes it (clip
+ * coefficient 1).  When dev_result->skip is 0 the out buffers hold exactly
+ * what zero_units_step would have left in the current ones (the caller swaps
+ * the tables); when it is 1 they hold unspecified values and the current
+ * state is unchanged.
+ *   units_host, units_dev  the prepared table of the current state: rows
+ *                          (contrib, ld) and master, m, v are read; grad is
+ *                          not used
+ *   out_host, out_dev      a prepared table with the same shards; its master,
+ *                          m, v and param16 are written, its other fields are
+ *                          not used
+ *   world_size, args, workspace, dev_result, stream: as zero_units_step
+ * Errors: as zero_units_step, plus ZERO_EINVAL for max_grad_norm > 0, a shard
+ * that differs between the tables, and a unit whose out buffers overlap its
+ * in buffers or one another.  Nothing is launched when a check fails.
+ */
+int zero_units_step_1pass(int32_t world_size, const zero_unit_buffers_t* units_host,
+                          const zero_unit_buffers_t* units_dev,
+                          const zero_unit_buffers_t* out_host,
+                          const zero_unit_buffers_t* out_dev, int32_t n_units,
+                          const zero_step_args_t* args, void* workspace, size_t ws_bytes,
+                          zero_step_result_t* dev_result, hipStream_t stream);
+
 typedef struct zero_scaler {
   double scale;            /* current loss scale */
   double growth, backoff;  /* e.g. 2.0 and 0.5 */

@@ -158,18 +158,22 @@ def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Opti
     return reports
 
 
-def run_units_all_ranks(w: synth.Workload, max_norm: Optional[float] = None) -> List[StepReport]:
+def run_units_all_ranks(w: synth.Workload, max_norm: Optional[float] = None,
+                        one_pass: bool = False) -> List[StepReport]:
     """Every rank of a unit layout on the GPU (zero_units_* through DeviceUnits)
     and in the oracle, all steps, with the exact all-reduce of the squared-norm
     integers and overflow flags between the ranks; every rank's g, result and
-    state compared bit for bit.  Returns rank 0's reports."""
+    state compared bit for bit.  With `one_pass` (no clipping) every rank runs
+    zero_units_step_1pass first, the all-reduce and zero_finalize follow, and
+    each rank adopts its new set unless the step was skipped; no g is written
+    or compared.  Returns rank 0's reports."""
     import zero_sharded_optimizer_rank_amd.abi as abi
     from zero_sharded_optimizer_rank_amd.units import DeviceUnits
 
     max_norm = w.max_grad_norm if max_norm is None else max_norm
     n = w.world_size
     up = orun.workload_unit_plan(w)
-    devs = [DeviceUnits(w, r) for r in range(n)]
+    devs = [DeviceUnits(w, r, one_pass=one_pass) for r in range(n)]
     for d in devs:
         d.load_initial_state()
     ost = [list(orun.unit_rank_initial_state(w, up, r)) for r in range(n)]
@@ -183,14 +187,20 @@ def run_units_all_ranks(w: synth.Workload, max_norm: Optional[float] = None) -> 
             d.load_contributions(step, scaler.scale)
         base = devs[0].args(scaler.t + 1, scaler.scale, max_norm=max_norm)
         for d in devs:
-            d.reduce_check(base)
+            if one_pass:
+                d.step_1pass(base)
+            else:
+                d.reduce_check(base)
         rs = [d.result() for d in devs]
         for r, d in enumerate(devs):
             a = d.args(scaler.t + 1, scaler.scale, max_norm=max_norm,
                        other_q=sum(rs[x].own_q for x in range(n) if x != r),
                        other_overflow=any(rs[x].overflow for x in range(n) if x != r))
             abi.zero_finalize(flat_plan, a, d.res, d.stream)
-            d.adam_apply(a)
+            if not one_pass:
+                d.adam_apply(a)
+            elif not d.result().skip:
+                d.adopt()
         # oracle
         sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, o_t + 1, n, o_scale)
         accs = [oracle.reduce_contributions(orun.unit_rank_contrib(w, up, r, step, o_scale))
@@ -205,7 +215,9 @@ def run_units_all_ranks(w: synth.Workload, max_norm: Optional[float] = None) -> 
             check_result(d.result(), fin, step)
             skipped = fin.skip
             g = oracle.unscale(accs[r], sc.inv32)
-            assert np.array_equal(d.fetch("grad").view(np.uint32), g.view(np.uint32)), (step, r)
+            if not one_pass:
+                assert np.array_equal(d.fetch("grad").view(np.uint32), g.view(np.uint32)), \
+                    (step, r)
             if not fin.skip:
                 p, m, v, h = oracle.adam_apply(g, ost[r][0], ost[r][1], ost[r][2], sc, fin.coef)
                 ost[r] = [p, m, v, h.view(np.uint16)]

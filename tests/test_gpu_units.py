@@ -74,18 +74,56 @@ def _feed_units_and_reduce(dev, step, scale, pos):
     return q_total, bad, cols
 
 
+@pytest.mark.parametrize("variant", ["config", "skip"])
+def test_tiny_fsdp_all_ranks_one_pass(variant):
+    """The unit single pass on all four tiny ranks: every rank's pass, then
+    the exact all-reduce and the adoption unless a rank overflowed."""
+    print(f"[tiny_fsdp one pass {variant}]", flush=True)
+    w = synth.TINY_FSDP
+    if variant == "skip":
+        w = dataclasses.replace(w, inject_step=2)
+    reports = run_units_all_ranks(w, 0.0, one_pass=True)
+    assert all(r.coef == 1.0 for r in reports)
+    if variant == "skip":
+        assert [r.skip for r in reports] == [s == 2 for s in range(1, w.steps + 1)]
+
+
+def test_units_one_pass_rejects_clipping_and_overlap():
+    import zero_sharded_optimizer_rank_amd.abi as abi
+    from zero_sharded_optimizer_rank_amd.units import DeviceUnits
+    w = synth.TINY_FSDP
+    d = DeviceUnits(w, 0, one_pass=True)
+    with pytest.raises(abi.ZeroError) as e:
+        d.step_1pass(d.args(1, w.loss_scale0, max_norm=1.0))
+    assert e.value.code == abi.ZERO_EINVAL
+    # an out table whose unit 0 writes over its own input state
+    bad = abi.unit_table(d.n_units)
+    for u in range(d.n_units):
+        bad[u] = d.table2[u]
+    bad[0].m = d.table[0].m
+    with pytest.raises(abi.ZeroError) as e:
+        abi.zero_units_step_1pass(w.world_size, d.table, d.table_dev, bad, d.table2_dev,
+                                  d.n_units, d.args(1, w.loss_scale0, max_norm=0.0), d.ws,
+                                  d.ws.numel(), d.res, d.stream)
+    assert e.value.code == abi.ZERO_EINVAL
+
+
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("w,rank", [pytest.param(synth.LLAMA3_8B_FSDP, 0, id="llama3_8b_fsdp-r0"),
-                                    pytest.param(synth.GPT2_FSDP, 1, id="gpt2_1p5b_fsdp-r1")])
-def test_units_full_rank(w, rank):
+@pytest.mark.parametrize("w,rank,one_pass", [
+    pytest.param(synth.LLAMA3_8B_FSDP, 0, False, id="llama3_8b_fsdp-r0"),
+    pytest.param(synth.GPT2_FSDP, 1, False, id="gpt2_1p5b_fsdp-r1"),
+    pytest.param(dataclasses.replace(synth.LLAMA3_8B_FSDP, max_grad_norm=0.0), 0, True,
+                 id="llama3_8b_fsdp-noclip-r0-1pass"),
+    pytest.param(synth.GPT2_FSDP, 1, True, id="gpt2_1p5b_fsdp-r1-1pass")])
+def test_units_full_rank(w, rank, one_pass):
     """A whole rank of a many-unit layout (34 units for Llama-3-8B, 50 for
     GPT-2), every step: whole-rank Q, norm, coef and skip from the C oracle on
     the same host chunks, and ~4k sampled elements bit for bit."""
     import zero_sharded_optimizer_rank_amd.abi as abi
     from zero_sharded_optimizer_rank_amd.units import DeviceUnits
 
-    print(f"[units full rank {w.name} rank {rank}]", flush=True)
-    dev = DeviceUnits(w, rank)
+    print(f"[units full rank {w.name} rank {rank} one_pass={one_pass}]", flush=True)
+    dev = DeviceUnits(w, rank, one_pass=one_pass)
     dev.load_initial_state()
     up = orun.workload_unit_plan(w)
     assert dev.plan.rank_shard == up.rank_shard
@@ -105,15 +143,21 @@ def test_units_full_rank(w, rank):
     o_scale, o_good, o_t = w.loss_scale0, 0, 0
     for step in range(1, w.steps + 1):
         q_all, bad_all, cols = _feed_units_and_reduce(dev, step, scaler.scale, pos)
-        dev.step(dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq))
+        if one_pass:
+            dev.step_1pass(dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq))
+        else:
+            dev.step(dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq))
         res = dev.result()
+        if one_pass and not res.skip:
+            dev.adopt()
         sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, o_t + 1, w.world_size,
                                  o_scale)
         fin = oracle.finalize(q_all, bad_all, sc.inv64, w.max_grad_norm, other_sq=other_sq)
         check_result(res, fin, step)
         acc = oracle.reduce_contributions(cols)
         g = oracle.unscale(acc, sc.inv32)
-        assert np.array_equal(_bits(dev.fetch_at("grad", pos)), _bits(g)), step
+        if not one_pass:
+            assert np.array_equal(_bits(dev.fetch_at("grad", pos)), _bits(g)), step
         if not fin.skip:
             op, om, ov, h = oracle.adam_apply(g, op, om, ov, sc, fin.coef)
             oh = h.view(np.uint16)

@@ -91,6 +91,11 @@
 #ifndef ZK_K12_LDS
 #define ZK_K12_LDS 8192
 #endif
+// The unit single pass keeps the unit reduce's two-wave workgroups (one
+// workgroup column for both) at the two-wave single pass's best cap.
+#ifndef ZK_K12U_LDS
+#define ZK_K12U_LDS 20480
+#endif
 // The bf16 single pass keeps two-wave workgroups (one tree partial per 512
 // elements, so the largest shard stays within the tree kernel's chunk) and
 // the two-wave single pass's best cap, 8 per CU.

@@ -606,6 +606,63 @@ int zero_units_step(int32_t world_size, const zero_unit_buffers_t* units_host,
   return zero_units_adam_apply(units_host, units_dev, n_units, args, dev_result, stream);
 }
 
+int zero_units_step_1pass(int32_t world_size, const zero_unit_buffers_t* units_host,
+                          const zero_unit_buffers_t* units_dev,
+                          const zero_unit_buffers_t* out_host,
+                          const zero_unit_buffers_t* out_dev, int32_t n_units,
+                          const zero_step_args_t* args, void* workspace, size_t ws_bytes,
+                          zero_step_result_t* dev_result, hipStream_t stream) {
+  g_err[0] = 0;
+  if (world_size < 1 || world_size > ZERO_MAX_RANKS)
+    return fail(ZERO_EINVAL, "world_size outside 1..%d", ZERO_MAX_RANKS);
+  int rc = check_adam_args(args);
+  if (rc) return rc;
+  if (args->max_grad_norm > 0.0)
+    return fail(ZERO_EINVAL,
+                "max_grad_norm > 0: clipping needs the whole norm before any update "
+                "(use the two-pass step)");
+  int64_t b1 = 0, b2 = 0, o1 = 0, o2 = 0;
+  rc = units_layout(nullptr, units_host, n_units, false, &b1, &b2);
+  if (!rc) rc = units_layout(nullptr, out_host, n_units, false, &o1, &o2);
+  if (rc) return rc;
+  if (n_units > 0 && (!units_dev || !out_dev)) return fail(ZERO_EINVAL, "a device table is NULL");
+  for (int32_t u = 0; u < n_units; ++u) {
+    const zero_unit_buffers_t& x = units_host[u];
+    const zero_unit_buffers_t& y = out_host[u];
+    if (x.shard != y.shard) return fail(ZERO_EINVAL, "unit %d: out table shard differs", u);
+    if (x.shard == 0) continue;
+    const size_t b4 = 4 * (size_t)x.shard, bh = 2 * (size_t)x.shard;
+    const void* ins[3] = {x.master, x.m, x.v};
+    const void* outs[4] = {y.master, y.m, y.v, y.param16};
+    const size_t ob[4] = {b4, b4, b4, bh};
+    for (int o = 0; o < 4; ++o) {
+      for (int i = 0; i < 3; ++i)
+        if (overlap(outs[o], ob[o], ins[i], b4))
+          return fail(ZERO_EINVAL, "unit %d: an output state buffer overlaps an input", u);
+      for (int q = 0; q < o; ++q)
+        if (overlap(outs[o], ob[o], outs[q], ob[q]))
+          return fail(ZERO_EINVAL, "unit %d: output state buffers overlap", u);
+    }
+  }
+  if (!dev_result) return fail(ZERO_EINVAL, "dev_result is NULL");
+  if (!aligned(dev_result, 8)) return fail(ZERO_EALIGN, "dev_result not 8-byte aligned");
+  if (!workspace) return fail(ZERO_EINVAL, "workspace is NULL");
+  if (!aligned(workspace, 16)) return fail(ZERO_EALIGN, "workspace not 16-byte aligned");
+  const size_t need = zk::workspace_bytes_for_blocks(b1);
+  if (ws_bytes < need) return fail(ZERO_ENOSPC, "workspace %zu bytes < %zu", ws_bytes, need);
+  zero_plan_t pl{0, world_size, 1, 0, 0};
+  const zk::FinalizeArgs fa = finalize_args(&pl, args);
+  if (b1 == 0)
+    return hip_status(zk::launch_finalize_empty(fa, dev_result, stream), "finalize launch");
+  rc = hip_status(zk::launch_units_reduce_adam_1pass(units_dev, out_dev, n_units, b1,
+                                                     world_size, (float)fa.inv64,
+                                                     adam_scalars(args), workspace, stream),
+                  "units single-pass launch");
+  if (rc) return rc;
+  return hip_status(zk::launch_partials_finalize(workspace, b1, fa, dev_result, stream),
+                    "finalize launch");
+}
+
 int zero_scaler_update(zero_scaler_t* s, int32_t skipped) {
   g_err[0] = 0;
   if (!s || !(s->scale > 0.0)) return fail(ZERO_EINVAL, "NULL scaler or scale <= 0");

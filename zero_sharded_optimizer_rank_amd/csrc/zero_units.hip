@@ -88,7 +88,42 @@ __global__ __launch_bounds__(ZK_K2_THREADS) void k2u_adam(
   }
 }
 
+// Single pass over all units (steps without clipping): `units` gives the
+// rows and the current state, `outs` (same shards, same workgroup columns)
+// the set that receives the new state and slot.
+static_assert(ZK_K1_QUADS == 1, "the unit single pass reuses the reduce's one-quad workgroups");
+__global__ __launch_bounds__(ZK_K1_THREADS) void k12u_reduce_adam(
+    const zero_unit_buffers_t* __restrict__ units, const zero_unit_buffers_t* __restrict__ outs,
+    int32_t n_units, int32_t n, float inv32, AdamScalars sc, Partial* __restrict__ partials,
+    uint32_t* __restrict__ ticket) {
+  const int64_t b = blockIdx.x;
+  if (b == 0 && threadIdx.x == 0) *ticket = 0u;
+  const int32_t u = find_unit(n_units, b, [&](int32_t i) { return units[i].reduce_block; });
+  const UnitBuffersGlobal& ub = ((const UnitBuffersGlobal*)units)[u];
+  const UnitBuffersGlobal& ob = ((const UnitBuffersGlobal*)outs)[u];
+  const StridedRows rows{(const uint16_t*)ub.contrib, ub.ld};
+  const StatePair st{(const float*)ub.master, (const float*)ub.m, (const float*)ub.v,
+                     (float*)ob.master,       (float*)ob.m,       (float*)ob.v,
+                     (uint16_t*)ob.param16};
+  uint64_t qlo = 0, qhi = 0;
+  uint32_t bad = 0;
+  const int64_t qd = (b - ub.reduce_block) * ZK_K1_THREADS + threadIdx.x;
+  reduce_adam_quad(rows, n, ub.shard, qd, inv32, st, sc, qlo, qhi, bad);
+  block_reduce<ZK_K1_THREADS>(qlo, qhi, bad);
+  if (threadIdx.x == 0) partials[b] = make_partial(qlo, qhi, bad);
+}
+
 }  // namespace
+
+int launch_units_reduce_adam_1pass(const zero_unit_buffers_t* units_dev,
+                                   const zero_unit_buffers_t* outs_dev, int32_t n_units,
+                                   int64_t blocks, int n, float inv32, const AdamScalars& sc,
+                                   void* workspace, hipStream_t stream) {
+  hipLaunchKernelGGL(k12u_reduce_adam, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), ZK_K12U_LDS,
+                     stream, units_dev, outs_dev, n_units, n, inv32, sc,
+                     (Partial*)workspace_partials(workspace), (uint32_t*)workspace);
+  return (int)hipGetLastError();
+}
 
 int launch_units_reduce(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
                         int n, float inv32, void* workspace, hipStream_t stream) {

@@ -26,7 +26,7 @@ CHUNK = 1 << 24
 
 class DeviceUnits:
     def __init__(self, w: synth.Workload, rank: int, device: str = "cuda:0",
-                 stream: Optional[torch.cuda.Stream] = None):
+                 stream: Optional[torch.cuda.Stream] = None, one_pass: bool = False):
         assert w.units is not None
         if w.dtype != "fp16":
             raise ValueError("the unit path takes fp16 contributions and slots")
@@ -54,16 +54,22 @@ class DeviceUnits:
         ld = row_pitch // 2
         st_pitch = round_up(4 * total, STAGGER_PERIOD) + STAGGER
         rows_end = round_up(n * row_pitch, STAGGER_PERIOD)
-        st_at = [rows_end + k * st_pitch for k in range(4)]
-        slots_at = round_up(rows_end + 4 * st_pitch, STAGGER_PERIOD) + STAGGER
+        # one_pass: master, m, v and the slots once more, for the set that
+        # zero_units_step_1pass writes
+        self.one_pass = one_pass
+        n_st = 7 if one_pass else 4
+        st_at = [rows_end + k * st_pitch for k in range(n_st)]
+        slots_at = round_up(rows_end + n_st * st_pitch, STAGGER_PERIOD) + STAGGER
         slot_elems = [GUARD + 8 + info.shard + GUARD for info in self.infos]
         # each unit's slot buffer starts on a 256-byte boundary, so a slot
         # with no misalignment (rank * S_u % 8 == 0) covers whole cache lines
         slot_offs = [0]
         for se in slot_elems[:-1]:
             slot_offs.append(slot_offs[-1] + round_up(se, ROW_ALIGN))
-        nbytes = slots_at + 2 * (slot_offs[-1] + round_up(slot_elems[-1], ROW_ALIGN)
-                                 if slot_elems else 0)
+        slots_bytes = 2 * (slot_offs[-1] + round_up(slot_elems[-1], ROW_ALIGN)
+                           if slot_elems else 0)
+        slots2_at = slots_at + round_up(slots_bytes, STAGGER_PERIOD) + STAGGER
+        nbytes = (slots2_at if one_pass else slots_at) + slots_bytes
         self.arena = torch.zeros(max(nbytes, 2), dtype=torch.uint8, device=self.device)
         a16 = self.arena.view(torch.int16)
         self.ld = ld
@@ -86,6 +92,11 @@ class DeviceUnits:
                 "slot_off": GUARD + mis, "shard": s, "ld": ld,
             }
             b["slot_buf"].fill_(GUARD_WORD)
+            if one_pass:
+                sa2 = slots2_at + 2 * slot_offs[u]
+                b.update(master2=f32(4), m2=f32(5), v2=f32(6),
+                         slot_buf2=self.arena[sa2:sa2 + 2 * slot_elems[u]].view(torch.int16))
+                b["slot_buf2"].fill_(GUARD_WORD)
             self.bufs.append(b)
             t = self.table[u]
             t.contrib = self.arena.data_ptr() + 2 * offs[u]
@@ -95,13 +106,28 @@ class DeviceUnits:
             t.param16 = b["slot_buf"].data_ptr() + 2 * b["slot_off"]
             t.shard = s
         self.reduce_blocks, self.adam_blocks = abi.zero_units_prepare(self.table, self.n_units)
-        raw = bytes(self.table)[:abi.UNIT_BUFFERS_BYTES * self.n_units] or b"\0"
-        self.table_dev = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(self.device)
+        self.table_dev = self._to_device(self.table)
+        self.table2 = self.table2_dev = None
+        if one_pass:
+            # the second table: the same units with the second state set
+            self.table2 = abi.unit_table(self.n_units)
+            for u, b in enumerate(self.bufs):
+                t, t2 = self.table[u], self.table2[u]
+                t2.contrib, t2.ld, t2.grad, t2.shard = t.contrib, t.ld, t.grad, t.shard
+                t2.master, t2.m = b["master2"].data_ptr(), b["m2"].data_ptr()
+                t2.v = b["v2"].data_ptr()
+                t2.param16 = b["slot_buf2"].data_ptr() + 2 * b["slot_off"]
+            abi.zero_units_prepare(self.table2, self.n_units)
+            self.table2_dev = self._to_device(self.table2)
         self.ws = torch.zeros(max(abi.zero_units_workspace_bytes(self.table, self.n_units), 16),
                               dtype=torch.uint8, device=self.device)
         self.res = torch.zeros(abi.RESULT_BYTES, dtype=torch.uint8, device=self.device)
         self._pin16 = torch.empty(CHUNK, dtype=torch.int16, pin_memory=True)
         self._pin32 = torch.empty(CHUNK, dtype=torch.float32, pin_memory=True)
+
+    def _to_device(self, table) -> torch.Tensor:
+        raw = bytes(table)[:abi.UNIT_BUFFERS_BYTES * self.n_units] or b"\0"
+        return torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(self.device)
 
     # ---------------------------------------------------------------- layout
     def unit_real(self, u: int) -> int:
@@ -121,10 +147,14 @@ class DeviceUnits:
 
     def guards_intact(self) -> bool:
         for u, b in enumerate(self.bufs):
-            lo = b["slot_buf"][:b["slot_off"]]
-            hi = b["slot_buf"][b["slot_off"] + b["shard"]:]
-            if not (bool((lo == GUARD_WORD).all().item()) and bool((hi == GUARD_WORD).all().item())):
-                return False
+            for key in ("slot_buf", "slot_buf2"):
+                if key not in b:
+                    continue
+                lo = b[key][:b["slot_off"]]
+                hi = b[key][b["slot_off"] + b["shard"]:]
+                if not (bool((lo == GUARD_WORD).all().item()) and
+                        bool((hi == GUARD_WORD).all().item())):
+                    return False
         return True
 
     # --------------------------------------------------------------- feeding
@@ -178,6 +208,26 @@ class DeviceUnits:
     def step(self, args):
         abi.zero_units_step(self.w.world_size, self.table, self.table_dev, self.n_units, args,
                             self.ws, self.ws.numel(), self.res, self.stream)
+
+    def step_1pass(self, args, res: Optional[torch.Tensor] = None):
+        """zero_units_step_1pass from the current set into the other one;
+        adopt() makes it current once the step is known not to have been
+        skipped."""
+        if not self.one_pass:
+            raise RuntimeError("these units were built without the second state set")
+        abi.zero_units_step_1pass(self.w.world_size, self.table, self.table_dev, self.table2,
+                                  self.table2_dev, self.n_units, args, self.ws, self.ws.numel(),
+                                  self.res if res is None else res, self.stream)
+
+    def adopt(self):
+        """Make the set the last step_1pass wrote the current one."""
+        if not self.one_pass:
+            raise RuntimeError("these units were built without the second state set")
+        self.table, self.table2 = self.table2, self.table
+        self.table_dev, self.table2_dev = self.table2_dev, self.table_dev
+        for b in self.bufs:
+            for x in ("master", "m", "v", "slot_buf"):
+                b[x], b[x + "2"] = b[x + "2"], b[x]
 
     def result(self) -> abi.zero_step_result_t:
         self.stream.synchronize()
