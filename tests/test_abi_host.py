@@ -200,3 +200,52 @@ def test_one_pass_argument_checks_without_launching():
     assert call(ins, outs, ins[1] + 2) == abi.ZERO_EINVAL                       # slot in m_in
     assert call(ins, [outs[0] + 4, outs[1], outs[2]], slot) == abi.ZERO_EALIGN
     assert call(ins, outs, slot, wsb=16) == abi.ZERO_ENOSPC
+
+
+def test_units_one_pass_argument_checks_without_launching():
+    """zero_units_step_1pass rejects clipping, a shard that differs between
+    the two tables and out buffers that overlap the unit's input state,
+    before anything reaches the GPU (the pointers are never used)."""
+    abi = _abi()
+    base = 1 << 32
+    shards = [1000, 24, 0]
+
+    def table(state_at):
+        t = abi.unit_table(len(shards))
+        for u, s in enumerate(shards):
+            x = t[u]
+            o = base + (u << 24)
+            x.contrib, x.ld, x.grad = o, 1024, o + (1 << 20)
+            x.master = state_at + (u << 24)
+            x.m, x.v = x.master + (1 << 16), x.master + (2 << 16)
+            x.param16 = x.master + (3 << 16)
+            x.shard = s
+        abi.zero_units_prepare(t, len(shards))
+        return t
+
+    ins, outs = table(base + (1 << 30)), table(base + (2 << 30))
+    ws_bytes = abi.zero_units_workspace_bytes(ins, len(shards))
+    ws, res, dev_in, dev_out = base + (3 << 30), base + (3 << 30) + (1 << 24), base, base + 64
+
+    def call(o, clip=0.0, n_units=len(shards)):
+        args = abi.step_args(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                             max_grad_norm=clip, loss_scale=1.0, step=1)
+        with pytest.raises(abi.ZeroError) as e:
+            abi.zero_units_step_1pass(2, ins, dev_in, o, dev_out, n_units, args, ws, ws_bytes,
+                                      res, 0)
+        return e.value.code
+
+    assert call(outs, clip=1.0) == abi.ZERO_EINVAL
+    other = table(base + (2 << 30))
+    other[1].shard = 32
+    abi.zero_units_prepare(other, len(shards))
+    assert call(other) == abi.ZERO_EINVAL                      # shard differs
+    alias = table(base + (2 << 30))
+    alias[0].v = ins[0].m                                      # out v over in m
+    assert call(alias) == abi.ZERO_EINVAL
+    alias = table(base + (2 << 30))
+    alias[1].param16 = alias[1].master + 4                      # slot over out master
+    assert call(alias) == abi.ZERO_EINVAL
+    unprepared = table(base + (2 << 30))
+    unprepared[2].reduce_block += 1
+    assert call(unprepared) == abi.ZERO_EINVAL
