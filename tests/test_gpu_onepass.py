@@ -192,9 +192,12 @@ def test_onepass_bf16_tiny_all_shards(variant):
         assert scaler.t == t
 
 
-def test_onepass_empty_shard():
+@pytest.mark.parametrize("fmt", ["fp16", "bf16"])
+def test_onepass_empty_shard(fmt):
     """S = 0: nothing to update; the result word is still written."""
     import zero_sharded_optimizer_rank_amd.abi as abi
+    step = (abi.zero_reduce_adam_step_1pass_bf16 if fmt == "bf16"
+            else abi.zero_reduce_adam_step_1pass)
     n = 4
     plan = abi.zero_plan_t(0, n, 1, 0, 0)
     ws = torch.zeros(abi.zero_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
@@ -202,7 +205,7 @@ def test_onepass_empty_shard():
     d = [torch.zeros(16, dtype=torch.float32, device="cuda") for _ in range(8)]
     args = abi.step_args(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
                          max_grad_norm=0.0, loss_scale=1.0, step=1)
-    abi.zero_reduce_adam_step_1pass(plan, 0, [d[0]] * n, *d[1:8], ws, ws.numel(), args, res)
+    step(plan, 0, [d[0]] * n, *d[1:8], ws, ws.numel(), args, res)
     torch.cuda.synchronize()
     r = abi.zero_step_result_t.from_buffer_copy(res.cpu().numpy().tobytes())
     assert r.own_q == 0 and r.norm == 0.0 and r.clip_coef == 1.0 and not r.skip
