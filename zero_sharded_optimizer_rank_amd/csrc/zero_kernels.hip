@@ -11,14 +11,18 @@
 //   bits), adds the other ranks' share and makes the clip / skip decision.
 // K2 (adam): mixed-precision AdamW on the shard and the fp16 cast into the
 //   all-gather slot (§10.6.2 steps 3 and 4), skipped as a whole on overflow.
+// K12 (reduce_adam, steps without clipping): K1 and K2 in one pass, reading
+//   the current master/m/v and writing a second set and slot, which the
+//   caller adopts only if KF finds the step not skipped; no gradient is
+//   written.  bf16 forms of K1, K2 and K12 sit at the end of the file.
 //
-// K1 and K2 stream every element once and use one-shot grids: each thread
+// K1, K2 and K12 stream every element once and use one-shot grids: each thread
 // owns one 4-element quad (no grid-stride loop), so workgroups are dispatched
 // in address order and retire as they finish; on MI355X this streams
 // measurably faster than persistent grids.  Every load or store instruction
 // of a wave covers 512 bytes to 1 KiB contiguous, with nontemporal hints.
 // Nothing here is a dense contraction, so no matrix cores are used; HBM
-// bandwidth bounds K1 and K2.  The per-quad bodies live in zero_device.h.
+// bandwidth bounds K1, K2 and K12.  The per-quad bodies live in zero_device.h.
 #include "zero_device.h"
 
 namespace zk {

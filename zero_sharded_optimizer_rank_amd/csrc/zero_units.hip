@@ -9,7 +9,9 @@
 // are dealt out unit by unit (zero_units_prepare records each unit's first
 // workgroup), so a workgroup finds its unit by a binary search and then runs
 // the same per-quad bodies as the flat kernels.  The squared norm and the
-// overflow flag cover all units together; the clip and skip are global.
+// overflow flag cover all units together; the clip and skip are global.  The
+// single pass over all units (steps without clipping) reads a second table
+// whose state buffers receive the update.
 #include <stddef.h>
 
 #include "zero_device.h"
