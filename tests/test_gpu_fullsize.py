@@ -108,8 +108,11 @@ def _cases():
         (synth.LLAMA3_8B_BF16, 0), (synth.LLAMA3_8B_BF16, 7),
         (MAX_SHARD, 1), (MAX_SHARD_BF16, 1),
     )]
-    # the single-pass step (unclipped workloads) as bench.py --one-pass times it
+    # the single-pass step (unclipped workloads) as bench.py --one-pass times it, and at
+    # the largest shard the ABI accepts (clipping off), fp16 and bf16
     cases += [pytest.param(synth.GPT2, r, True, id=f"gpt2_1p5b-r{r}-1pass") for r in (0, 1)]
+    cases += [pytest.param(dataclasses.replace(w, max_grad_norm=0.0), 1, True,
+                           id=f"{w.name}-r1-1pass") for w in (MAX_SHARD, MAX_SHARD_BF16)]
     return cases
 
 
