@@ -265,3 +265,66 @@ def test_onepass_rejects_clipping_and_overlap():
     assert e.value.code == abi.ZERO_ENOSPC
     after = [d.fetch(x) for x in ("master", "m", "v", "slot")]
     assert all(np.array_equal(x, y) for x, y in zip(before, after))
+
+
+@pytest.mark.parametrize("value", [np.inf, -np.inf, np.nan])
+@pytest.mark.parametrize("pos", ["first", "last", "tail"])
+def test_onepass_nonfinite_skips(value, pos):
+    """A non-finite contribution at the first, the last real and a tail
+    element: the result word matches the oracle's, the step is skipped, and
+    the current set (not adopted) is bitwise the state before the step."""
+    import oracle
+    from zero_sharded_optimizer_rank_amd.shard import DeviceShard
+    print(f"[onepass nonfinite {value} at {pos}]", flush=True)
+    w = synth.TINY
+    p = orun.workload_plan(w)
+    rank, count = 3, p.shard  # rank 3 holds the padding element
+    j = {"first": 0, "last": p.real(rank) - 1, "tail": count - 5}[pos]
+    q = 2
+    d = DeviceShard(w, rank, 0, count, one_pass=True)
+    d.load_initial_state()
+    d.load_contributions(1, w.loss_scale0)
+    d.contrib[q, j] = int(np.array([value], dtype=np.float16).view(np.int16)[0])
+    before = {x: d.fetch(x).copy() for x in ("master", "m", "v", "slot")}
+    d.step_1pass(d.args(1, w.loss_scale0))
+    res = d.result()
+    c = orun.shard_contrib(w, p, rank, 1, w.loss_scale0, 0, count)
+    c[q, j] = np.array([value], dtype=np.float16).view(np.uint16)[0]
+    acc = oracle.reduce_contributions(c)
+    sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, 1, w.world_size,
+                             w.loss_scale0)
+    fin = oracle.finalize(oracle.exact_sq_units(acc), oracle.nonfinite(acc), sc.inv64, 0.0)
+    check_result(res, fin, 1)
+    assert res.skip and res.overflow
+    for x, arr in before.items():
+        assert np.array_equal(d.fetch(x), arr), x
+    assert d.guards_intact()
+
+
+def test_onepass_extreme_magnitudes():
+    """N = 64 with every contribution at +-65504 (and one subnormal): the
+    largest sums the pass sees; result word and state against the oracle."""
+    import oracle
+    from zero_sharded_optimizer_rank_amd.shard import DeviceShard
+    print("[onepass extreme magnitudes]", flush=True)
+    w = dataclasses.replace(synth.TINY, world_size=64)
+    p = orun.workload_plan(w)
+    count = p.shard
+    d = DeviceShard(w, 0, 0, count, one_pass=True)
+    d.load_initial_state()
+    c = np.full((64, d.ld), 65504.0, dtype=np.float16)
+    c[:, ::2] = -65504.0
+    c[5, 7] = 2.0**-24
+    d.contrib.copy_(torch.from_numpy(c.view(np.int16)))
+    d.step_1pass(d.args(1, 1.0))
+    res = d.result()
+    pm, m, v, h = orun.initial_state(w, p, 0, 0, count)
+    sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, 1, 64, 1.0)
+    out = oracle.shard_step(c[:, :count].view(np.uint16), pm, m, v, h, sc, 0.0)
+    check_result(res, out.fin, 1)
+    assert not res.skip
+    d.adopt()
+    for name, want in (("master", out.p), ("m", out.m), ("v", out.v),
+                       ("slot", out.h.view(np.uint16))):
+        got = d.fetch(name)
+        assert np.array_equal(got.view(np.uint8), np.ascontiguousarray(want).view(np.uint8)), name
