@@ -282,6 +282,31 @@ int zero_reduce_adam_step_1pass(const zero_plan_t* plan, int32_t rank,
                                 void* workspace, size_t ws_bytes, const zero_step_args_t* args,
                                 zero_step_result_t* dev_result, hipStream_t stream);
 
+/*
+ * zero_slot_restore / zero_slot_restore_bf16: let a single pass write the live
+ * slot in place.  The single pass never reads the slot, so param16_slot_out
+ * may be the live slot itself (flat16 + rank * S) instead of a second flat
+ * buffer; a skipped step then leaves garbage there.  After the step's final
+ * finalize (zero_reduce_adam_step_1pass's own, or zero_finalize after the
+ * exchange between ranks), this call rewrites the slot as the fp16 (bf16)
+ * cast of `master`, rounded to nearest even, if dev_result->skip is set, and
+ * does nothing otherwise; no host synchronisation is needed.  Pass the set
+ * the step read (master_in), which a skip leaves unchanged: since every step
+ * leaves the slot equal to the cast of the master, this gives back the slot's
+ * content before the step.
+ *   master        device [S] fp32, 4-byte aligned, read
+ *   param16_slot  device [S] 16-bit slot, 2-byte aligned, rewritten on a skip
+ *   dev_result    device, as written by the step's finalize; skip is read
+ * Errors: ZERO_EINVAL (plan, rank, NULL pointers, slot overlapping master),
+ * ZERO_EALIGN, ZERO_EHIP.
+ */
+int zero_slot_restore(const zero_plan_t* plan, int32_t rank, const float* master,
+                      uint16_t* param16_slot, const zero_step_result_t* dev_result,
+                      hipStream_t stream);
+int zero_slot_restore_bf16(const zero_plan_t* plan, int32_t rank, const float* master,
+                           uint16_t* param_bf16_slot, const zero_step_result_t* dev_result,
+                           hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* bf16 variant: bfloat16 gradient contributions and parameter slot, no loss
  * scaling needed (the tutorial's §4.3 suggests bf16 where the hardware has it,

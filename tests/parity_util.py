@@ -85,13 +85,15 @@ def other_overflow_at(w: synth.Workload, step: int, flat_begin: int, count: int)
 def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Optional[int] = None,
                fused: bool = True, strict: bool = True,
                ws_fill: Optional[int] = None, offload: Optional[dict] = None,
-               one_pass: bool = False) -> List[StepReport]:
+               one_pass: bool = False, in_place_slot: bool = False) -> List[StepReport]:
     """Run `steps` steps of the workload on one window of rank's shard on the
     GPU and in the oracle; compare every step.  With `offload` (OffloadShard
     keyword arguments) the update runs in the offload form: host state, PCIe
     pipeline.  With `one_pass` (unclipped workloads) each step is
     zero_reduce_adam_step_1pass into the second state set, adopted only when
-    the step was not skipped; no gradient is written, so none is compared."""
+    the step was not skipped; no gradient is written, so none is compared.
+    With `in_place_slot` as well, the pass writes the live slot and
+    zero_slot_restore follows every step."""
     import zero_sharded_optimizer_rank_amd.abi as abi
     from zero_sharded_optimizer_rank_amd.shard import DeviceShard, OffloadShard
 
@@ -119,7 +121,9 @@ def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Opti
         dev.load_contributions(step, scaler.scale)
         args = dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq, other_overflow=ovf_other)
         if one_pass:
-            dev.step_1pass(args)
+            dev.step_1pass(args, in_place_slot=in_place_slot)
+            if in_place_slot:
+                dev.restore_slot()
         elif fused:
             dev.step(args)
         else:
@@ -127,7 +131,7 @@ def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Opti
             dev.adam_apply(args)
         res = dev.result()
         if one_pass and not res.skip:
-            dev.adopt()
+            dev.adopt(swap_slot=not in_place_slot)
         # oracle
         c = orun.shard_contrib(w, p, rank, step, o_scale, begin, count)
         sc = oracle.step_scalars(w.lr, w.betas[0], w.betas[1], w.eps, w.weight_decay, o_t + 1,

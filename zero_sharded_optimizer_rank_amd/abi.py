@@ -123,6 +123,9 @@ _SIGNATURES = {
                                                         _P(_vp), _vp, _vp, _vp, _vp, _vp, _vp,
                                                         _vp, _vp, ctypes.c_size_t,
                                                         _P(zero_step_args_t), _vp, _vp]),
+    "zero_slot_restore": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _vp, _vp, _vp, _vp]),
+    "zero_slot_restore_bf16": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _vp, _vp, _vp,
+                                              _vp]),
     "zero_reduce_check_bf16": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _P(_vp),
                                               _P(zero_step_args_t), _vp, _vp, ctypes.c_size_t,
                                               _vp, _vp]),
@@ -312,6 +315,17 @@ def zero_reduce_adam_step_1pass_bf16(plan, rank, contrib, master_in, m_in, v_in,
                                                   _addr(workspace), ws_bytes,
                                                   ctypes.byref(args), _addr(dev_result),
                                                   _stream(stream)))
+
+
+def zero_slot_restore(plan, rank, master, param16_slot, dev_result, stream=None):
+    _check(lib().zero_slot_restore(ctypes.byref(plan), rank, _addr(master), _addr(param16_slot),
+                                   _addr(dev_result), _stream(stream)))
+
+
+def zero_slot_restore_bf16(plan, rank, master, param_bf16_slot, dev_result, stream=None):
+    _check(lib().zero_slot_restore_bf16(ctypes.byref(plan), rank, _addr(master),
+                                        _addr(param_bf16_slot), _addr(dev_result),
+                                        _stream(stream)))
 
 
 def zero_reduce_check_bf16(plan, rank, contrib, args, grad_out, workspace, ws_bytes, dev_result,

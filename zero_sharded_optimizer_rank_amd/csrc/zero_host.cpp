@@ -377,6 +377,36 @@ int zero_reduce_adam_step_1pass_bf16(const zero_plan_t* plan, int32_t rank,
                     "reduce_adam_1pass_bf16 launch");
 }
 
+static int slot_restore(const zero_plan_t* plan, int32_t rank, const float* master,
+                        uint16_t* slot, const zero_step_result_t* dev_result, bool bf16,
+                        hipStream_t stream) {
+  g_err[0] = 0;
+  int rc = check_plan_rank(plan, rank);
+  if (rc) return rc;
+  if (!dev_result) return fail(ZERO_EINVAL, "dev_result is NULL");
+  if (!aligned(dev_result, 8)) return fail(ZERO_EALIGN, "dev_result not 8-byte aligned");
+  if (plan->shard == 0) return ZERO_OK;
+  if (!master || !slot) return fail(ZERO_EINVAL, "NULL state pointer");
+  if (!aligned(master, 4)) return fail(ZERO_EALIGN, "master not 4-byte aligned");
+  if (!aligned(slot, 2)) return fail(ZERO_EALIGN, "slot not 2-byte aligned");
+  if (overlap(master, 4 * (size_t)plan->shard, slot, 2 * (size_t)plan->shard))
+    return fail(ZERO_EINVAL, "slot overlaps master");
+  return hip_status(zk::launch_slot_restore(master, slot, plan->shard, bf16, dev_result, stream),
+                    "slot restore launch");
+}
+
+int zero_slot_restore(const zero_plan_t* plan, int32_t rank, const float* master,
+                      uint16_t* param16_slot, const zero_step_result_t* dev_result,
+                      hipStream_t stream) {
+  return slot_restore(plan, rank, master, param16_slot, dev_result, false, stream);
+}
+
+int zero_slot_restore_bf16(const zero_plan_t* plan, int32_t rank, const float* master,
+                           uint16_t* param_bf16_slot, const zero_step_result_t* dev_result,
+                           hipStream_t stream) {
+  return slot_restore(plan, rank, master, param_bf16_slot, dev_result, true, stream);
+}
+
 int zero_reduce_check_bf16(const zero_plan_t* plan, int32_t rank, const uint16_t* const* contrib,
                            const zero_step_args_t* args, float* grad_out, void* workspace,
                            size_t ws_bytes, zero_step_result_t* dev_result, hipStream_t stream) {

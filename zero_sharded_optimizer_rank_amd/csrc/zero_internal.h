@@ -13,6 +13,7 @@ constexpr int kThreads = 256;        // threads per workgroup (four 64-wide wave
 constexpr int kFinBlocks = 256;      // most workgroups of the partial-sum kernel
 constexpr size_t kTicketBytes = 256; // ticket word (armed by the reduce kernel), padded
 constexpr size_t kPartialBytes = 16;
+constexpr int64_t kRestoreBlocks = 2048;  // most workgroups of the slot restore
 
 // fp64 inputs of the norm / clip / skip decision.
 struct FinalizeArgs {
@@ -59,6 +60,10 @@ int launch_reduce_adam_1pass(const uint16_t* const* contrib, int n, int64_t shar
                              float* master_out, float* m_out, float* v_out, uint16_t* slot_out,
                              const AdamScalars& sc, void* workspace, const FinalizeArgs& fa,
                              zero_step_result_t* res, hipStream_t stream);
+
+// Recast the slot from the master when res->skip (16-bit fp16 or bf16 slot).
+int launch_slot_restore(const float* master, uint16_t* slot, int64_t shard, bool bf16,
+                        const zero_step_result_t* res, hipStream_t stream);
 
 // bf16 path (the norm is a fixed pairwise fp64 tree; see zero_device.h).
 int64_t k1_blocks_bf16(int64_t shard);

@@ -150,6 +150,21 @@ __global__ __launch_bounds__(ZK_K2_THREADS) void k2_adam_bf16(
   }
 }
 
+// Slot restore after a skipped single pass that wrote the live slot: the
+// slot is the 16-bit cast of the master, so recasting the unchanged master
+// gives back its content before the step.  A no-op unless res->skip; a small
+// grid-stride grid, so that the common no-op costs one short launch.
+template <Fmt F>
+__global__ __launch_bounds__(kThreads) void k_slot_restore(const float* __restrict__ master,
+                                                           uint16_t* __restrict__ slot,
+                                                           int64_t shard,
+                                                           const zero_step_result_t* __restrict__ res) {
+  if (!res->skip) return;
+  for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < shard;
+       j += (int64_t)gridDim.x * kThreads)
+    slot[j] = (uint16_t)from_f32<F>(master[j]);
+}
+
 }  // namespace
 
 int64_t k1_blocks_bf16(int64_t shard) {
@@ -300,6 +315,20 @@ int launch_reduce_adam_1pass_bf16(const uint16_t* const* contrib, int n, int64_t
   const int e = (int)hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_tree_finalize_bf16(workspace, blocks, fa, res, stream);
+}
+
+int launch_slot_restore(const float* master, uint16_t* slot, int64_t shard, bool bf16,
+                        const zero_step_result_t* res, hipStream_t stream) {
+  int64_t blocks = (shard + kThreads - 1) / kThreads;
+  if (blocks > kRestoreBlocks) blocks = kRestoreBlocks;
+  if (blocks < 1) blocks = 1;
+  if (bf16)
+    hipLaunchKernelGGL(k_slot_restore<Fmt::BF16>, dim3((uint32_t)blocks), dim3(kThreads), 0,
+                       stream, master, slot, shard, res);
+  else
+    hipLaunchKernelGGL(k_slot_restore<Fmt::F16>, dim3((uint32_t)blocks), dim3(kThreads), 0,
+                       stream, master, slot, shard, res);
+  return (int)hipGetLastError();
 }
 
 int launch_finalize_bf16(const FinalizeArgs& fa, zero_step_result_t* res, hipStream_t stream) {

@@ -198,26 +198,38 @@ class DeviceShard:
                                   self.m, self.v, self.slot_ptr(), self.grad, self.ws,
                                   self.ws.numel(), args, self.res, self.stream)
 
-    def step_1pass(self, args, res: Optional[torch.Tensor] = None):
-        """zero_reduce_adam_step_1pass from the current master/m/v and slot into
-        the other set; adopt() makes that set current once the step is known
-        not to have been skipped."""
+    def step_1pass(self, args, res: Optional[torch.Tensor] = None, in_place_slot: bool = False):
+        """zero_reduce_adam_step_1pass from the current master/m/v into the
+        other set; adopt() makes that set current once the step is known not to
+        have been skipped.  The new slot goes to the second slot buffer, or with
+        `in_place_slot` into the live slot, which restore_slot() then repairs
+        if the step was skipped."""
         if not self.one_pass:
             raise RuntimeError("this shard was built without the second state set")
         f = abi.zero_reduce_adam_step_1pass_bf16 if self.bf16 else abi.zero_reduce_adam_step_1pass
-        f(
-            self.plan, self.rank_in_plan, self.contrib_ptrs(), self.master, self.m, self.v,
-            self.master2, self.m2, self.v2, self.slot_buf2.data_ptr() + 2 * self.slot_off,
-            self.ws, self.ws.numel(), args, self.res if res is None else res, self.stream)
+        slot_out = self.slot_ptr() if in_place_slot else \
+            self.slot_buf2.data_ptr() + 2 * self.slot_off
+        f(self.plan, self.rank_in_plan, self.contrib_ptrs(), self.master, self.m, self.v,
+          self.master2, self.m2, self.v2, slot_out, self.ws, self.ws.numel(), args,
+          self.res if res is None else res, self.stream)
 
-    def adopt(self):
-        """Make the set the last step_1pass wrote the current one."""
+    def restore_slot(self, res: Optional[torch.Tensor] = None):
+        """zero_slot_restore on the live slot from the current master: a no-op
+        unless the step in the result word was skipped."""
+        f = abi.zero_slot_restore_bf16 if self.bf16 else abi.zero_slot_restore
+        f(self.plan, self.rank_in_plan, self.master, self.slot_ptr(),
+          self.res if res is None else res, self.stream)
+
+    def adopt(self, swap_slot: bool = True):
+        """Make the set the last step_1pass wrote the current one (with
+        swap_slot=False after an in-place slot step)."""
         if not self.one_pass:
             raise RuntimeError("this shard was built without the second state set")
         self.master, self.master2 = self.master2, self.master
         self.m, self.m2 = self.m2, self.m
         self.v, self.v2 = self.v2, self.v
-        self.slot_buf, self.slot_buf2 = self.slot_buf2, self.slot_buf
+        if swap_slot:
+            self.slot_buf, self.slot_buf2 = self.slot_buf2, self.slot_buf
 
     @property
     def rank_in_plan(self) -> int:
