@@ -218,6 +218,9 @@ def main():
     ap.add_argument("--one-pass", action="store_true",
                     help="time zero_reduce_adam_step_1pass (steps without clipping: reduce and "
                          "update in one pass into a second state set, 2N + 26 bytes per element)")
+    ap.add_argument("--in-place-slot", action="store_true",
+                    help="--one-pass on a flat shard: write the live slot and call "
+                         "zero_slot_restore after every step (timed with the step)")
     ap.add_argument("--no-clip", action="store_true",
                     help="turn the workload's gradient clipping off (a variant, named in the "
                          "config; needed for --one-pass on workloads that clip)")
@@ -400,18 +403,33 @@ def one_pass_main(a, w):
     # step must have applied, so adopting each new set unconditionally is right
     res = torch.zeros((a.warmup + a.steps, abi.RESULT_BYTES), dtype=torch.uint8,
                       device=dev.device)
+    in_place = a.in_place_slot and w.units is None
+
+    def one_step(t, r):
+        if in_place:
+            dev.step_1pass(dev.args(t, w.loss_scale0, other_sq=other_sq), res=r,
+                           in_place_slot=True)
+            dev.restore_slot(res=r)
+        else:
+            dev.step_1pass(dev.args(t, w.loss_scale0, other_sq=other_sq), res=r)
+
+    def adopt():
+        if w.units is None:
+            dev.adopt(swap_slot=not in_place)
+        else:
+            dev.adopt()
+
     for i in range(a.warmup):
-        dev.step_1pass(dev.args(i + 1, w.loss_scale0, other_sq=other_sq), res=res[i])
-        dev.adopt()
+        one_step(i + 1, res[i])
+        adopt()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
         ev[i][0].record(stream)
-        dev.step_1pass(dev.args(a.warmup + i + 1, w.loss_scale0, other_sq=other_sq),
-                       res=res[a.warmup + i])
+        one_step(a.warmup + i + 1, res[a.warmup + i])
         ev[i][1].record(stream)
-        dev.adopt()
+        adopt()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     raw = res.cpu().numpy()
@@ -435,6 +453,8 @@ def one_pass_main(a, w):
                                f"{w.dtype} contributions and slot, fp32 master/m/v in two sets, "
                                f"single-pass step"
                                + (f", {n_units} FSDP units" if w.units else "")
+                               + (", slot in place with zero_slot_restore each step"
+                                  if in_place else "")
                                + (" (clipping turned off)" if a.no_clip else " (no clipping)"),
                    "world_size_simulated": n, "shard": S, "psi": w.psi},
         "step_ms_p10_p50_p90": [per_step[int(q * (len(per_step) - 1))] for q in (0.1, 0.5, 0.9)],
@@ -444,7 +464,8 @@ def one_pass_main(a, w):
                      "traffic": traffic_for(w.name + "_1pass", kname)},
         "kernels": {kname: {"ms": k_ms, "bytes_per_param": bpp, "bytes": bpp * S,
                                         "gbps": gbps,
-                                        "note": "event pair spans the pass and the finalize"}},
+                                        "note": "event pair spans the pass and the finalize"
+                                                + (" and the slot restore" if in_place else "")}},
         "calibration_copy": calib,
         "setup_s": setup_s,
         "kernel_hash": kernel_hash(),
