@@ -538,6 +538,21 @@ int zero_units_step_1pass(int32_t world_size, const zero_unit_buffers_t* units_h
                           const zero_step_args_t* args, void* workspace, size_t ws_bytes,
                           zero_step_result_t* dev_result, hipStream_t stream);
 
+/*
+ * zero_units_slot_restore: zero_slot_restore over all units in one launch,
+ * for a unit single pass whose out table points param16 at the live unit
+ * slots: if dev_result->skip, every unit's param16 is rewritten as the fp16
+ * cast of its master (round to nearest even); otherwise nothing happens.
+ *   units_host, units_dev  the prepared table of the current state (the one
+ *                          the pass read), with param16 at the live slots
+ *   dev_result             as written by the step's final finalize
+ * Errors: ZERO_EINVAL (a table not prepared, NULL pointers, a slot that
+ * overlaps its unit's master), ZERO_EALIGN, ZERO_EHIP.
+ */
+int zero_units_slot_restore(const zero_unit_buffers_t* units_host,
+                            const zero_unit_buffers_t* units_dev, int32_t n_units,
+                            const zero_step_result_t* dev_result, hipStream_t stream);
+
 typedef struct zero_scaler {
   double scale;            /* current loss scale */
   double growth, backoff;  /* e.g. 2.0 and 0.5 */

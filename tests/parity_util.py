@@ -163,21 +163,23 @@ def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Opti
 
 
 def run_units_all_ranks(w: synth.Workload, max_norm: Optional[float] = None,
-                        one_pass: bool = False) -> List[StepReport]:
+                        one_pass: bool = False, in_place_slot: bool = False) -> List[StepReport]:
     """Every rank of a unit layout on the GPU (zero_units_* through DeviceUnits)
     and in the oracle, all steps, with the exact all-reduce of the squared-norm
     integers and overflow flags between the ranks; every rank's g, result and
     state compared bit for bit.  With `one_pass` (no clipping) every rank runs
     zero_units_step_1pass first, the all-reduce and zero_finalize follow, and
     each rank adopts its new set unless the step was skipped; no g is written
-    or compared.  Returns rank 0's reports."""
+    or compared.  With `in_place_slot` the pass writes the live unit slots and
+    zero_units_slot_restore follows the finalize.  Returns rank 0's reports."""
     import zero_sharded_optimizer_rank_amd.abi as abi
     from zero_sharded_optimizer_rank_amd.units import DeviceUnits
 
     max_norm = w.max_grad_norm if max_norm is None else max_norm
     n = w.world_size
     up = orun.workload_unit_plan(w)
-    devs = [DeviceUnits(w, r, one_pass=one_pass) for r in range(n)]
+    devs = [DeviceUnits(w, r, one_pass=one_pass, in_place_slot=in_place_slot)
+            for r in range(n)]
     for d in devs:
         d.load_initial_state()
     ost = [list(orun.unit_rank_initial_state(w, up, r)) for r in range(n)]
@@ -203,7 +205,10 @@ def run_units_all_ranks(w: synth.Workload, max_norm: Optional[float] = None,
             abi.zero_finalize(flat_plan, a, d.res, d.stream)
             if not one_pass:
                 d.adam_apply(a)
-            elif not d.result().skip:
+                continue
+            if in_place_slot:
+                d.restore_slot()
+            if not d.result().skip:
                 d.adopt()
         # oracle
         sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, o_t + 1, n, o_scale)

@@ -171,6 +171,8 @@ def test_random_configuration_onepass_matches_oracle(seed):
 def test_random_unit_layout_one_pass_matches_oracle(seed):
     """The unit single pass on random unit layouts with clipping off."""
     w = dataclasses.replace(random_unit_workload(100 + seed), max_grad_norm=0.0)
+    in_place = seed % 2 == 1  # half of them write the live slots and restore them
     print(f"[random units one pass {seed}] N={w.world_size} numels={w.numels} units={w.units} "
-          f"scale={w.loss_scale0} sigma={w.sigma} inject={w.inject_step}", flush=True)
-    run_units_all_ranks(w, one_pass=True)
+          f"scale={w.loss_scale0} sigma={w.sigma} inject={w.inject_step} in_place={in_place}",
+          flush=True)
+    run_units_all_ranks(w, one_pass=True, in_place_slot=in_place)

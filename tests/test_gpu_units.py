@@ -88,6 +88,19 @@ def test_tiny_fsdp_all_ranks_one_pass(variant):
         assert [r.skip for r in reports] == [s == 2 for s in range(1, w.steps + 1)]
 
 
+@pytest.mark.parametrize("variant", ["config", "skip"])
+def test_tiny_fsdp_all_ranks_one_pass_in_place_slot(variant):
+    """The unit single pass writing the live unit slots, with
+    zero_units_slot_restore after the all-reduce's finalize on every rank."""
+    print(f"[tiny_fsdp one pass in place {variant}]", flush=True)
+    w = synth.TINY_FSDP
+    if variant == "skip":
+        w = dataclasses.replace(w, inject_step=2)
+    reports = run_units_all_ranks(w, 0.0, one_pass=True, in_place_slot=True)
+    if variant == "skip":
+        assert [r.skip for r in reports] == [s == 2 for s in range(1, w.steps + 1)]
+
+
 def test_units_one_pass_rejects_clipping_and_overlap():
     import zero_sharded_optimizer_rank_amd.abi as abi
     from zero_sharded_optimizer_rank_amd.units import DeviceUnits

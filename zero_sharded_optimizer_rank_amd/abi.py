@@ -166,6 +166,8 @@ _SIGNATURES = {
                                              _P(zero_unit_buffers_t), _vp, ctypes.c_int32,
                                              _P(zero_step_args_t), _vp, ctypes.c_size_t, _vp,
                                              _vp]),
+    "zero_units_slot_restore": (ctypes.c_int, [_P(zero_unit_buffers_t), _vp, ctypes.c_int32,
+                                               _vp, _vp]),
     "zero_scaler_update": (ctypes.c_int, [_P(zero_scaler_t), ctypes.c_int32]),
     "zero_last_error": (ctypes.c_char_p, []),
 }
@@ -446,6 +448,11 @@ def zero_units_step_1pass(world_size, table_host, table_dev, out_host, out_dev, 
                                        _addr(out_dev), n_units, ctypes.byref(args),
                                        _addr(workspace), ws_bytes, _addr(dev_result),
                                        _stream(stream)))
+
+
+def zero_units_slot_restore(table_host, table_dev, n_units, dev_result, stream=None):
+    _check(lib().zero_units_slot_restore(table_host, _addr(table_dev), n_units,
+                                         _addr(dev_result), _stream(stream)))
 
 
 def new_scaler(scale: float, growth: float = 2.0, backoff: float = 0.5, min_scale: float = 1.0,

@@ -693,6 +693,29 @@ int zero_units_step_1pass(int32_t world_size, const zero_unit_buffers_t* units_h
                     "finalize launch");
 }
 
+int zero_units_slot_restore(const zero_unit_buffers_t* units_host,
+                            const zero_unit_buffers_t* units_dev, int32_t n_units,
+                            const zero_step_result_t* dev_result, hipStream_t stream) {
+  g_err[0] = 0;
+  int64_t b1 = 0, b2 = 0;
+  int rc = units_layout(nullptr, units_host, n_units, false, &b1, &b2);
+  if (rc) return rc;
+  if (n_units > 0 && !units_dev) return fail(ZERO_EINVAL, "units_dev is NULL");
+  if (!dev_result) return fail(ZERO_EINVAL, "dev_result is NULL");
+  if (!aligned(dev_result, 8)) return fail(ZERO_EALIGN, "dev_result not 8-byte aligned");
+  int64_t max_shard = 0;
+  for (int32_t u = 0; u < n_units; ++u) {
+    const zero_unit_buffers_t& x = units_host[u];
+    if (x.shard > max_shard) max_shard = x.shard;
+    if (x.shard > 0 && overlap(x.master, 4 * (size_t)x.shard, x.param16, 2 * (size_t)x.shard))
+      return fail(ZERO_EINVAL, "unit %d: slot overlaps master", u);
+  }
+  if (max_shard == 0) return ZERO_OK;
+  return hip_status(zk::launch_units_slot_restore(units_dev, n_units, max_shard, dev_result,
+                                                  stream),
+                    "units slot restore launch");
+}
+
 int zero_scaler_update(zero_scaler_t* s, int32_t skipped) {
   g_err[0] = 0;
   if (!s || !(s->scale > 0.0)) return fail(ZERO_EINVAL, "NULL scaler or scale <= 0");

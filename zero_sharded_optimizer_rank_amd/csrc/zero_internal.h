@@ -86,6 +86,9 @@ int launch_units_reduce(const zero_unit_buffers_t* units_dev, int32_t n_units, i
                         int n, float inv32, void* workspace, hipStream_t stream);
 int launch_units_adam(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
                       const AdamScalars& sc, const zero_step_result_t* res, hipStream_t stream);
+int launch_units_slot_restore(const zero_unit_buffers_t* units_dev, int32_t n_units,
+                              int64_t max_shard, const zero_step_result_t* res,
+                              hipStream_t stream);
 int launch_units_reduce_adam_1pass(const zero_unit_buffers_t* units_dev,
                                    const zero_unit_buffers_t* outs_dev, int32_t n_units,
                                    int64_t blocks, int n, float inv32, const AdamScalars& sc,

@@ -115,7 +115,34 @@ __global__ __launch_bounds__(ZK_K1_THREADS) void k12u_reduce_adam(
   if (threadIdx.x == 0) partials[b] = make_partial(qlo, qhi, bad);
 }
 
+// Slot restore over all units (see the flat k_slot_restore): a no-op unless
+// the step was skipped; then every unit's slot is recast from its master.
+__global__ __launch_bounds__(kThreads) void k_units_slot_restore(
+    const zero_unit_buffers_t* __restrict__ units, int32_t n_units,
+    const zero_step_result_t* __restrict__ res) {
+  if (!res->skip) return;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int32_t u = 0; u < n_units; ++u) {
+    const UnitBuffersGlobal& ub = ((const UnitBuffersGlobal*)units)[u];
+    const float* master = (const float*)ub.master;
+    uint16_t* slot = (uint16_t*)ub.param16;
+    for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < ub.shard; j += stride)
+      slot[j] = (uint16_t)f2h(master[j]);
+  }
+}
+
 }  // namespace
+
+int launch_units_slot_restore(const zero_unit_buffers_t* units_dev, int32_t n_units,
+                              int64_t max_shard, const zero_step_result_t* res,
+                              hipStream_t stream) {
+  int64_t blocks = (max_shard + kThreads - 1) / kThreads;
+  if (blocks > kRestoreBlocks) blocks = kRestoreBlocks;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_units_slot_restore, dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
+                     units_dev, n_units, res);
+  return (int)hipGetLastError();
+}
 
 int launch_units_reduce_adam_1pass(const zero_unit_buffers_t* units_dev,
                                    const zero_unit_buffers_t* outs_dev, int32_t n_units,

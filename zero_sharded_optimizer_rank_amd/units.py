@@ -26,7 +26,8 @@ CHUNK = 1 << 24
 
 class DeviceUnits:
     def __init__(self, w: synth.Workload, rank: int, device: str = "cuda:0",
-                 stream: Optional[torch.cuda.Stream] = None, one_pass: bool = False):
+                 stream: Optional[torch.cuda.Stream] = None, one_pass: bool = False,
+                 in_place_slot: bool = False):
         assert w.units is not None
         if w.dtype != "fp16":
             raise ValueError("the unit path takes fp16 contributions and slots")
@@ -57,6 +58,9 @@ class DeviceUnits:
         # one_pass: master, m, v and the slots once more, for the set that
         # zero_units_step_1pass writes
         self.one_pass = one_pass
+        # with in_place_slot both tables point param16 at the live slots, and
+        # restore_slot() repairs them after a skipped single pass
+        self.in_place_slot = one_pass and in_place_slot
         n_st = 7 if one_pass else 4
         st_at = [rows_end + k * st_pitch for k in range(n_st)]
         slots_at = round_up(rows_end + n_st * st_pitch, STAGGER_PERIOD) + STAGGER
@@ -116,7 +120,8 @@ class DeviceUnits:
                 t2.contrib, t2.ld, t2.grad, t2.shard = t.contrib, t.ld, t.grad, t.shard
                 t2.master, t2.m = b["master2"].data_ptr(), b["m2"].data_ptr()
                 t2.v = b["v2"].data_ptr()
-                t2.param16 = b["slot_buf2"].data_ptr() + 2 * b["slot_off"]
+                t2.param16 = t.param16 if self.in_place_slot else \
+                    b["slot_buf2"].data_ptr() + 2 * b["slot_off"]
             abi.zero_units_prepare(self.table2, self.n_units)
             self.table2_dev = self._to_device(self.table2)
         self.ws = torch.zeros(max(abi.zero_units_workspace_bytes(self.table, self.n_units), 16),
@@ -219,14 +224,21 @@ class DeviceUnits:
                                   self.table2_dev, self.n_units, args, self.ws, self.ws.numel(),
                                   self.res if res is None else res, self.stream)
 
+    def restore_slot(self, res: Optional[torch.Tensor] = None):
+        """zero_units_slot_restore on the live slots from the current masters:
+        a no-op unless the step in the result word was skipped."""
+        abi.zero_units_slot_restore(self.table, self.table_dev, self.n_units,
+                                    self.res if res is None else res, self.stream)
+
     def adopt(self):
         """Make the set the last step_1pass wrote the current one."""
         if not self.one_pass:
             raise RuntimeError("these units were built without the second state set")
         self.table, self.table2 = self.table2, self.table
         self.table_dev, self.table2_dev = self.table2_dev, self.table_dev
+        swapped = ("master", "m", "v") if self.in_place_slot else ("master", "m", "v", "slot_buf")
         for b in self.bufs:
-            for x in ("master", "m", "v", "slot_buf"):
+            for x in swapped:
                 b[x], b[x + "2"] = b[x + "2"], b[x]
 
     def result(self) -> abi.zero_step_result_t:
