@@ -249,3 +249,23 @@ def test_units_one_pass_argument_checks_without_launching():
     unprepared = table(base + (2 << 30))
     unprepared[2].reduce_block += 1
     assert call(unprepared) == abi.ZERO_EINVAL
+
+
+def test_slot_restore_argument_checks_without_launching():
+    """zero_slot_restore rejects a bad rank, a NULL or misaligned buffer and a
+    slot that overlaps the master before anything reaches the GPU."""
+    abi = _abi()
+    S = 1000
+    plan = abi.zero_plan_t(S, 2, 1, S, 2 * S)
+    base = 1 << 32
+    master, slot, res = base, base + (1 << 20), base + (2 << 20)
+    for f in (abi.zero_slot_restore, abi.zero_slot_restore_bf16):
+        for args, code in (((plan, 2, master, slot, res), abi.ZERO_EINVAL),
+                           ((plan, 0, 0, slot, res), abi.ZERO_EINVAL),
+                           ((plan, 0, master, slot, 0), abi.ZERO_EINVAL),
+                           ((plan, 0, master + 2, slot, res), abi.ZERO_EALIGN),
+                           ((plan, 0, master, slot + 1, res), abi.ZERO_EALIGN),
+                           ((plan, 0, master, master + 4 * S - 2, res), abi.ZERO_EINVAL)):
+            with pytest.raises(abi.ZeroError) as e:
+                f(*args)
+            assert e.value.code == code, (f.__name__, args)

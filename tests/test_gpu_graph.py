@@ -108,3 +108,52 @@ def test_onepass_graph_replays_match_eager():
         for k in got:
             assert np.array_equal(got[k].view(np.uint8), eager[i][k].view(np.uint8)), (i, k)
         assert dg.guards_intact()
+
+
+def test_onepass_in_place_slot_graph_replays_match_eager():
+    """A single pass writing the live slot plus zero_slot_restore, captured
+    twice as one graph (set 0 -> set 1 -> set 0), replays to the same bits as
+    eager calls; the restore reads the skip flag on the device."""
+    from zero_sharded_optimizer_rank_amd.shard import DeviceShard
+
+    w = synth.GPT2
+    rank, begin, count = 1, 777, 200_003
+    print("[graph one pass in place]", flush=True)
+    s_eager, s_graph = torch.cuda.Stream(), torch.cuda.Stream()
+    de = DeviceShard(w, rank, begin, count, stream=s_eager, one_pass=True)
+    dg = DeviceShard(w, rank, begin, count, stream=s_graph, one_pass=True)
+    for d in (de, dg):
+        d.load_initial_state()
+        d.load_contributions(1, w.loss_scale0)
+    args = de.args(1, w.loss_scale0)
+
+    def two_steps(d):
+        for _ in range(2):
+            d.step_1pass(args, in_place_slot=True)
+            d.restore_slot()
+            d.adopt(swap_slot=False)
+
+    def snap(d):
+        d.stream.synchronize()
+        out = {x: d.fetch(x).copy() for x in ("master", "m", "v", "slot")}
+        out["res"] = d.res.cpu().numpy().copy()
+        return out
+
+    eager = []
+    for _ in range(3):
+        two_steps(de)
+        eager.append(snap(de))
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=s_graph):
+        two_steps(dg)
+    torch.cuda.synchronize()
+    for i in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        got = snap(dg)
+        junk = torch.randn(1 << 20, device="cuda").sum().item()
+        assert np.isfinite(junk)
+        for k in got:
+            assert np.array_equal(got[k].view(np.uint8), eager[i][k].view(np.uint8)), (i, k)
+        assert dg.guards_intact()
