@@ -245,6 +245,31 @@ int zero_reduce_adam_step(const zero_plan_t* plan, int32_t rank, const uint16_t*
                           hipStream_t stream);
 
 /*
+ * zero_reduce_adam_step_noalloc: zero_reduce_adam_step for callers that
+ * cannot allocate device memory or pass a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * reduce's workspace comes from a device array the library holds, one per
+ * GPU, of 36 MiB + 4352 B: enough for shards of up to ZERO_NOALLOC_MAX_SHARD
+ * elements.  The call allocates nothing; the first call on a device resolves
+ * that device's array address (a runtime symbol lookup, no allocation), so
+ * make one call per device before capturing it in a graph.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (other streams, other threads) race and must not be issued; calls in
+ * sequence on one stream are safe.  Kernels, results and bits are those of
+ * zero_reduce_adam_step.
+ * Arguments: as zero_reduce_adam_step without workspace and ws_bytes.
+ * Errors: as zero_reduce_adam_step, plus ZERO_ENOSPC for a shard above
+ * ZERO_NOALLOC_MAX_SHARD (checked before anything touches the GPU), and
+ * ZERO_EHIP if the device or the array's address cannot be obtained.
+ */
+#define ZERO_NOALLOC_MAX_SHARD ((int64_t)1207959552) /* 9 * 2^27 */
+int zero_reduce_adam_step_noalloc(const zero_plan_t* plan, int32_t rank,
+                                  const uint16_t* const* contrib, float* master, float* m,
+                                  float* v, uint16_t* param16_slot, float* grad_out,
+                                  const zero_step_args_t* args, zero_step_result_t* dev_result,
+                                  hipStream_t stream);
+
+/*
  * zero_reduce_adam_step_1pass: the whole step in one streaming pass, for steps
  * without gradient clipping (args->max_grad_norm <= 0), e.g. a GPT-2-sized
  * model trained with dynamic loss scaling and no clipping.  Pages: as

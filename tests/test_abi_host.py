@@ -269,3 +269,33 @@ def test_slot_restore_argument_checks_without_launching():
             with pytest.raises(abi.ZeroError) as e:
                 f(*args)
             assert e.value.code == code, (f.__name__, args)
+
+
+def test_noalloc_step_argument_checks_without_launching():
+    """zero_reduce_adam_step_noalloc rejects a shard above its scratch limit,
+    a bad rank and NULL or misaligned buffers before it touches the GPU (the
+    pointers are never used, and no device exists here)."""
+    abi = _abi()
+    base = 1 << 32
+    rows = [base, base + (1 << 20)]
+    master, m, v, slot, grad, res = (base + (k << 20) for k in range(2, 8))
+    args = abi.step_args(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                         max_grad_norm=1.0, loss_scale=1.0, step=1)
+
+    def call(plan, rank=0, r=rows, g=grad, sl=slot, rs=res):
+        with pytest.raises(abi.ZeroError) as e:
+            abi.zero_reduce_adam_step_noalloc(plan, rank, r, master, m, v, sl, g, args, rs, 0)
+        return e.value.code, str(e.value)
+
+    big = abi.ZERO_NOALLOC_MAX_SHARD + 8
+    code, msg = call(abi.zero_plan_t(2 * big, 2, 1, big, 2 * big))
+    assert code == abi.ZERO_ENOSPC and "scratch" in msg
+    S = 1000
+    plan = abi.zero_plan_t(S, 2, 1, S, 2 * S)
+    assert call(plan, rank=2)[0] == abi.ZERO_EINVAL
+    assert call(plan, r=[base, 0])[0] == abi.ZERO_EINVAL
+    assert call(plan, r=[base, base + 8])[0] == abi.ZERO_EALIGN
+    assert call(plan, g=0)[0] == abi.ZERO_EINVAL
+    assert call(plan, g=grad + 4)[0] == abi.ZERO_EALIGN
+    assert call(plan, sl=slot + 1)[0] == abi.ZERO_EALIGN
+    assert call(plan, rs=0)[0] == abi.ZERO_EINVAL

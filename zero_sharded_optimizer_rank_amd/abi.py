@@ -19,6 +19,7 @@ LIB_PATH = os.environ.get("ZERO_SHARD_LIB") or os.path.join(HERE, "libzero_shard
 ZERO_OK, ZERO_EINVAL, ZERO_EALIGN, ZERO_ENOSPC, ZERO_EHIP = 0, -1, -2, -3, -4
 ZERO_MAX_RANKS = 64
 ZERO_MAX_SHARD = 0x7FFFFFF8
+ZERO_NOALLOC_MAX_SHARD = 9 << 27
 
 
 class ZeroError(RuntimeError):
@@ -115,6 +116,9 @@ _SIGNATURES = {
     "zero_reduce_adam_step": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _P(_vp), _vp, _vp,
                                              _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                              _P(zero_step_args_t), _vp, _vp]),
+    "zero_reduce_adam_step_noalloc": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _P(_vp),
+                                                     _vp, _vp, _vp, _vp, _vp,
+                                                     _P(zero_step_args_t), _vp, _vp]),
     "zero_reduce_adam_step_1pass": (ctypes.c_int, [_P(zero_plan_t), ctypes.c_int32, _P(_vp),
                                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                    ctypes.c_size_t, _P(zero_step_args_t), _vp,
@@ -294,6 +298,15 @@ def zero_reduce_adam_step(plan, rank, contrib, master, m, v, param16_slot, grad_
                                        _addr(master), _addr(m), _addr(v), _addr(param16_slot),
                                        _addr(grad_out), _addr(workspace), ws_bytes,
                                        ctypes.byref(args), _addr(dev_result), _stream(stream)))
+
+
+def zero_reduce_adam_step_noalloc(plan, rank, contrib, master, m, v, param16_slot, grad_out, args,
+                                  dev_result, stream=None):
+    _check(lib().zero_reduce_adam_step_noalloc(ctypes.byref(plan), rank, _ptr_array(contrib),
+                                               _addr(master), _addr(m), _addr(v),
+                                               _addr(param16_slot), _addr(grad_out),
+                                               ctypes.byref(args), _addr(dev_result),
+                                               _stream(stream)))
 
 
 def zero_reduce_adam_step_1pass(plan, rank, contrib, master_in, m_in, v_in, master_out, m_out,

@@ -42,19 +42,22 @@ def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     kobj = os.path.join(BUILD_DIR, "zero_kernels.o")
     uobj = os.path.join(BUILD_DIR, "zero_units.o")
+    nobj = os.path.join(BUILD_DIR, "zero_noalloc.o")
     hobj = os.path.join(BUILD_DIR, "zero_host.o")
     oobj = os.path.join(BUILD_DIR, "zero_offload.o")
     _run([HIPCC, "-x", "hip", *COMMON, *FP_FLAGS, *DEVICE_FLAGS, "-c",
           os.path.join(CSRC, "zero_kernels.hip"), "-o", kobj])
     _run([HIPCC, "-x", "hip", *COMMON, *FP_FLAGS, *DEVICE_FLAGS, "-c",
           os.path.join(CSRC, "zero_units.hip"), "-o", uobj])
+    _run([HIPCC, "-x", "hip", *COMMON, *FP_FLAGS, *DEVICE_FLAGS, "-c",
+          os.path.join(CSRC, "zero_noalloc.hip"), "-o", nobj])
     _run([HIPCC, *COMMON, "-ffp-contract=off", "-c", os.path.join(CSRC, "zero_host.cpp"),
           "-o", hobj])
     # host Adam of the offload form: IEEE fp32, no contraction, errno-free sqrt
     _run([HIPCC, *COMMON, "-ffp-contract=off", "-fno-math-errno", "-pthread", "-c",
           os.path.join(CSRC, "zero_offload.cpp"), "-o", oobj])
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", kobj, uobj, hobj, oobj,
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", kobj, uobj, nobj, hobj, oobj,
           "-o", tmp])
     os.replace(tmp, LIB)
     # measurement-only copy kernel, in a library of its own

@@ -100,6 +100,18 @@ zk::AdamScalars adam_scalars(const zero_step_args_t* a) {
   return s;
 }
 
+// The N contribution rows of a reduce.
+int check_rows(const zero_plan_t* plan, const uint16_t* const* contrib) {
+  if (plan->shard == 0) return ZERO_OK;
+  if (!contrib) return fail(ZERO_EINVAL, "contrib is NULL");
+  for (int64_t r = 0; r < plan->world_size; ++r) {
+    if (!contrib[r]) return fail(ZERO_EINVAL, "contrib[%lld] is NULL", (long long)r);
+    if (!aligned(contrib[r], 16))
+      return fail(ZERO_EALIGN, "contrib[%lld] not 16-byte aligned", (long long)r);
+  }
+  return ZERO_OK;
+}
+
 // Contribution rows, workspace and result of a reduce.
 int check_reduce_inputs(const zero_plan_t* plan, const uint16_t* const* contrib, void* workspace,
                         size_t ws_bytes, zero_step_result_t* dev_result) {
@@ -109,16 +121,9 @@ int check_reduce_inputs(const zero_plan_t* plan, const uint16_t* const* contrib,
   if (!aligned(workspace, 16)) return fail(ZERO_EALIGN, "workspace not 16-byte aligned");
   const size_t need = zk::workspace_bytes(plan->shard);
   if (ws_bytes < need) return fail(ZERO_ENOSPC, "workspace %zu bytes < %zu", ws_bytes, need);
-  if (plan->shard > 0) {
-    if (!contrib) return fail(ZERO_EINVAL, "contrib is NULL");
-    for (int64_t r = 0; r < plan->world_size; ++r) {
-      if (!contrib[r]) return fail(ZERO_EINVAL, "contrib[%lld] is NULL", (long long)r);
-      if (!aligned(contrib[r], 16))
-        return fail(ZERO_EALIGN, "contrib[%lld] not 16-byte aligned", (long long)r);
-    }
-  }
-  return ZERO_OK;
+  return check_rows(plan, contrib);
 }
+
 
 int check_reduce_ptrs(const zero_plan_t* plan, const uint16_t* const* contrib, float* grad_out,
                       void* workspace, size_t ws_bytes, zero_step_result_t* dev_result) {
