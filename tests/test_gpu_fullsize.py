@@ -1,18 +1,26 @@
 """GPU parity at the workloads' full shard sizes, in the launch configuration
 bench.py times (the whole shard of the rank).
 
-Every step of each workload runs on the GPU.  The oracle checks:
+Every step of each workload runs on the GPU, and the oracle checks it over
+the whole shard, every element:
   * the exact squared-norm integer (fp16) or the pairwise fp64 tree (bf16),
-    overflow flag, norm, clip coefficient and skip decision of the whole
-    shard (computed by the C form of the oracle's reduce statistics from the
-    same host-generated input chunks that are copied to the device; for bf16
-    each chunk is an aligned power-of-two subtree, and the roots are summed
-    by the oracle's pairwise tree);
-  * g, master, m, v and the fp16 slot at ~4k sampled elements (first, last,
-    random, and around an injected inf), computed one by one by the numpy
-    oracle, bit for bit, with the state carried across steps.
+    overflow flag, norm, clip coefficient and skip decision, computed by the
+    C form of the oracle's reduce statistics from the same host-generated
+    input chunks that are copied to the device (for bf16 each chunk is an
+    aligned power-of-two subtree, and the roots are summed by the oracle's
+    pairwise tree);
+  * g (two-pass form), master, m, v and the 16-bit slot, bit for bit: the C
+    form of the oracle's unscale and Adam update (pinned bit for bit to the
+    numpy definitions on the CPU) runs on the host over the whole shard, with
+    the state carried across steps, and every device array is fetched chunk
+    by chunk and compared with it.
+
+With ZERO_FULLSIZE_SAMPLED=1 in the environment the state is compared only at
+~4k sampled elements per step (first, last, random, around 2^30 and 2^31 and
+an injected inf), computed by the numpy oracle: a faster mode for iterating.
 """
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -27,6 +35,9 @@ from parity_util import check_result, compare_state, other_overflow_at, StepRepo
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
+
+SAMPLED = os.environ.get("ZERO_FULLSIZE_SAMPLED", "") not in ("", "0")
+FETCH = 1 << 26  # elements per device-to-host comparison chunk
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -52,10 +63,11 @@ def _sample_indices(w, rank, shard, k=4096):
     return np.array(sorted(idx), dtype=np.int64)
 
 
-def _feed_and_reduce(dev, step, scale, idx):
+def _feed_and_reduce(dev, step, scale, inv32, idx=None, g_out=None):
     """Generate the step's contributions chunk by chunk on the host, copy each
     chunk to the device, and reduce the same chunk with the C oracle.  Returns
-    (Q or, for bf16, the tree value; overflow; contributions at idx)."""
+    (Q or, for bf16, the tree value; overflow; contributions at idx or None).
+    With g_out, the oracle's g = f32(acc * inv32) of every element goes there."""
     w, n, count = dev.w, dev.w.world_size, dev.count
     chunk = (1 << 28) // (2 * n)  # 256 MiB of host staging
     bf16 = w.dtype == "bf16"
@@ -64,7 +76,7 @@ def _feed_and_reduce(dev, step, scale, idx):
     host = torch.empty((n, chunk), dtype=torch.int16, pin_memory=True)
     hnp = host.numpy().view(np.uint16)
     q_total, bad = 0, False
-    cols = np.zeros((n, idx.size), dtype=np.uint16)
+    cols = None if idx is None else np.zeros((n, idx.size), dtype=np.uint16)
     for c0 in range(0, count, chunk):
         k = min(chunk, count - c0)
         for q in range(n):
@@ -79,12 +91,52 @@ def _feed_and_reduce(dev, step, scale, idx):
             qc, bc = fast.reduce_stats(hnp, k)
             q_total += qc
         bad |= bc
-        sel = (idx >= c0) & (idx < c0 + k)
-        cols[:, sel] = hnp[:, idx[sel] - c0]
+        if g_out is not None:
+            fast.reduce_unscale(hnp, inv32, count=k, bf16=bf16, out=g_out[c0:c0 + k])
+        if cols is not None:
+            sel = (idx >= c0) & (idx < c0 + k)
+            cols[:, sel] = hnp[:, idx[sel] - c0]
         dev.stream.synchronize()
     if bf16:
         return oracle.pairwise_sum_f64(np.array(roots)), bad, cols
     return q_total, bad, cols
+
+
+class _Fetcher:
+    """Device array -> host chunks through one pinned buffer."""
+
+    def __init__(self, dev):
+        self.dev = dev
+        self.buf32 = torch.empty(min(FETCH, max(dev.count, 1)), dtype=torch.float32,
+                                 pin_memory=True)
+        self.buf16 = self.buf32.view(torch.int16)
+
+    def compare(self, rep, name, want):
+        """Bitwise mismatches of the whole device array `name` against `want`;
+        on a mismatch, also the 1e-6 / 1-ulp bar over the offending chunk."""
+        d = self.dev
+        t = {"grad": d.grad, "master": d.master, "m": d.m, "v": d.v}.get(name)
+        t = d.slot if name == "slot" else t[:d.count]
+        mism, worst = 0, 0.0
+        for s in range(0, d.count, FETCH):
+            k = min(FETCH, d.count - s)
+            buf = self.buf16[:k] if name == "slot" else self.buf32[:k]
+            with torch.cuda.stream(d.stream):
+                buf.copy_(t[s:s + k], non_blocking=True)
+            d.stream.synchronize()
+            got = buf.numpy().view(np.uint16 if name == "slot" else np.float32)
+            ref = want[s:s + k]
+            bad = fast.count_unequal(got, ref)
+            if bad:
+                mism += bad
+                sub = StepReport(rep.step, rep.skip, rep.coef)
+                try:
+                    compare_state(sub, name, got.copy(), ref.copy())
+                finally:
+                    worst = max(worst, sub.max_rel.get(name, float("inf")))
+        rep.mismatches[name] = mism
+        rep.max_rel[name] = worst
+        return mism
 
 
 # The largest shard the ABI accepts (2^31 - 8 elements) at N = 2: element
@@ -116,30 +168,53 @@ def _cases():
     return cases
 
 
+def _initial_host_state(w, flat_begin, count):
+    """Oracle state of the whole shard: seeded fp32 masters, m = v = 0, and
+    the 16-bit cast of the masters."""
+    p = np.empty(count, dtype=np.float32)
+    for s in range(0, count, 1 << 26):
+        k = min(1 << 26, count - s)
+        synth.masters(w, flat_begin + s, k, out=p[s:s + k])
+    return p, np.zeros(count, np.float32), np.zeros(count, np.float32), \
+        fast.cast16(p, bf16=w.dtype == "bf16")
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("w,rank,one_pass", _cases())
 def test_full_size_shard(w, rank, one_pass):
     import zero_sharded_optimizer_rank_amd.abi as abi
     from zero_sharded_optimizer_rank_amd.shard import DeviceShard
 
-    print(f"[full size {w.name} rank {rank}{' one pass' if one_pass else ''}]", flush=True)
+    mode = "sampled" if SAMPLED else "every element"
+    print(f"[full size {w.name} rank {rank}{' one pass' if one_pass else ''}, {mode}]",
+          flush=True)
     dev = DeviceShard(w, rank, one_pass=one_pass)
     dev.load_initial_state()
     p = orun.workload_plan(w)
     assert dev.count == p.shard and dev.flat_begin == rank * p.shard
-    idx = _sample_indices(w, rank, p.shard)
-    flat = rank * p.shard + idx
-    op = np.array([synth.masters(w, int(e), 1)[0] for e in flat], dtype=np.float32)
-    om, ov = np.zeros_like(op), np.zeros_like(op)
     bf16 = w.dtype == "bf16"
-    oh = orun.half_copy(w, op)
+    if SAMPLED:
+        idx = _sample_indices(w, rank, p.shard)
+        flat = rank * p.shard + idx
+        op = np.array([synth.masters(w, int(e), 1)[0] for e in flat], dtype=np.float32)
+        om, ov = np.zeros_like(op), np.zeros_like(op)
+        oh = orun.half_copy(w, op)
+        hg = None
+    else:
+        idx = None
+        op, om, ov, oh = _initial_host_state(w, dev.flat_begin, dev.count)
+        hg = np.empty(dev.count, dtype=np.float32)
+        fetch = _Fetcher(dev)
     other_sq = w.other_sq(p.real(rank)) if w.other_ranks_from_config else 0.0
     scaler = abi.new_scaler(w.loss_scale0)
     o_scale, o_good, o_t = w.loss_scale0, 0, 0
     skips = []
     for step in range(1, w.steps + 1):
+        assert scaler.scale == o_scale
+        sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, o_t + 1, w.world_size,
+                                 o_scale)
         ovf_other = other_overflow_at(w, step, dev.flat_begin, dev.count)
-        q_all, bad_all, cols = _feed_and_reduce(dev, step, scaler.scale, idx)
+        q_all, bad_all, cols = _feed_and_reduce(dev, step, scaler.scale, sc.inv32, idx, hg)
         args = dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq, other_overflow=ovf_other)
         if one_pass:
             dev.step_1pass(args)
@@ -148,27 +223,34 @@ def test_full_size_shard(w, rank, one_pass):
         res = dev.result()
         if one_pass and not res.skip:
             dev.adopt()
-        sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, o_t + 1, w.world_size,
-                                 o_scale)
         fin_fn = oracle.finalize_bf16 if bf16 else oracle.finalize
         fin = fin_fn(q_all, bad_all, sc.inv64, w.max_grad_norm, other_sq=other_sq,
                      other_overflow=ovf_other)
         check_result(res, fin, step)
-        acc = (oracle.reduce_contributions_bf16 if bf16 else oracle.reduce_contributions)(cols)
-        g = oracle.unscale(acc, sc.inv32)
-        if not one_pass:  # the single pass writes no gradient
-            assert np.array_equal(dev.fetch("grad", idx).view(np.uint32),
-                                  g.view(np.uint32)), step
-        if not fin.skip:
-            op, om, ov, h = oracle.adam_apply(g, op, om, ov, sc, fin.coef)
-            oh = oracle.f32_to_bf16(op) if bf16 else h.view(np.uint16)
         rep = StepReport(step, fin.skip, float(fin.coef))
-        for name, want in (("master", op), ("m", om), ("v", ov), ("slot", oh)):
-            compare_state(rep, name, dev.fetch(name, idx), want)
-        assert all(x == 0 for x in rep.mismatches.values()), (step, rep.mismatches)
+        if SAMPLED:
+            acc = (oracle.reduce_contributions_bf16 if bf16 else oracle.reduce_contributions)(cols)
+            g = oracle.unscale(acc, sc.inv32)
+            if not one_pass:  # the single pass writes no gradient
+                assert np.array_equal(dev.fetch("grad", idx).view(np.uint32),
+                                      g.view(np.uint32)), step
+            if not fin.skip:
+                op, om, ov, h = oracle.adam_apply(g, op, om, ov, sc, fin.coef)
+                oh = oracle.f32_to_bf16(op) if bf16 else h.view(np.uint16)
+            for name, want in (("master", op), ("m", om), ("v", ov), ("slot", oh)):
+                compare_state(rep, name, dev.fetch(name, idx), want)
+        else:
+            if not one_pass:  # the single pass writes no gradient
+                assert fetch.compare(rep, "grad", hg) == 0, (step, rep.max_rel)
+            if not fin.skip:
+                fast.adam_update(hg, op, om, ov, oh, sc, fin.coef, bf16=bf16)
+            for name, want in (("master", op), ("m", om), ("v", ov), ("slot", oh)):
+                fetch.compare(rep, name, want)
+        assert all(x == 0 for x in rep.mismatches.values()), (step, rep.mismatches, rep.max_rel)
         assert dev.guards_intact()
         print(f"  step {step}: skip={fin.skip} coef={float(fin.coef):.6g} norm={fin.norm:.6g} "
-              f"stat={q_all if bf16 else q_all.bit_length()}", flush=True)
+              f"stat={q_all if bf16 else q_all.bit_length()} compared="
+              f"{idx.size if SAMPLED else dev.count} x {sorted(rep.mismatches)}", flush=True)
         skips.append(fin.skip)
         abi.zero_scaler_update(scaler, bool(res.skip))
         o_scale, o_good = oracle.scaler_update(o_scale, o_good, fin.skip)
@@ -179,3 +261,4 @@ def test_full_size_shard(w, rank, one_pass):
                                                     if i != w.inject_step - 1)
     del dev
     torch.cuda.empty_cache()
+

@@ -91,44 +91,44 @@ def test_offload_errors():
                                     pytest.param(synth.GPT2, 1, id="gpt2_1p5b-r1")])
 def test_offload_full_size(w, rank):
     """Whole shards in the configuration bench.py --offload times: the exact
-    norm, decisions and ~4k sampled elements of host state and device slot."""
+    norm and decisions, and every element of g and the device slot and of
+    the host master, m and v, against the C form of the oracle's update."""
     import zero_sharded_optimizer_rank_amd.abi as abi
     from zero_sharded_optimizer_rank_amd.shard import OffloadShard
-    from test_gpu_fullsize import _feed_and_reduce, _sample_indices
+    from oracle import fast
+    from test_gpu_fullsize import _Fetcher, _feed_and_reduce, _initial_host_state
 
     print(f"[offload full size {w.name} rank {rank}]", flush=True)
     dev = OffloadShard(w, rank)
     dev.load_initial_state()
     p = orun.workload_plan(w)
-    idx = _sample_indices(w, rank, p.shard)
-    flat = rank * p.shard + idx
-    op = np.array([synth.masters(w, int(e), 1)[0] for e in flat], dtype=np.float32)
-    om, ov = np.zeros_like(op), np.zeros_like(op)
-    oh = op.astype(np.float16).view(np.uint16)
+    op, om, ov, oh = _initial_host_state(w, dev.flat_begin, dev.count)
+    hg = np.empty(dev.count, dtype=np.float32)
+    fetch = _Fetcher(dev)
     other_sq = w.other_sq(p.real(rank)) if w.other_ranks_from_config else 0.0
     scaler = abi.new_scaler(w.loss_scale0)
     o_scale, o_good, o_t = w.loss_scale0, 0, 0
     for step in range(1, w.steps + 1):
         ovf_other = other_overflow_at(w, step, dev.flat_begin, dev.count)
-        q_all, bad_all, cols = _feed_and_reduce(dev, step, scaler.scale, idx)
-        res = dev.step(dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq,
-                                other_overflow=ovf_other))
         sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, o_t + 1, w.world_size,
                                  o_scale)
+        q_all, bad_all, _ = _feed_and_reduce(dev, step, scaler.scale, sc.inv32, g_out=hg)
+        res = dev.step(dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq,
+                                other_overflow=ovf_other))
         fin = oracle.finalize(q_all, bad_all, sc.inv64, w.max_grad_norm, other_sq=other_sq,
                               other_overflow=ovf_other)
         check_result(res, fin, step)
-        g = oracle.unscale(oracle.reduce_contributions(cols), sc.inv32)
-        assert np.array_equal(dev.fetch("grad", idx).view(np.uint32), g.view(np.uint32)), step
-        if not fin.skip:
-            op, om, ov, h = oracle.adam_apply(g, op, om, ov, sc, fin.coef)
-            oh = h.view(np.uint16)
         rep = StepReport(step, fin.skip, float(fin.coef))
-        for name, want in (("master", op), ("m", om), ("v", ov), ("slot", oh)):
-            compare_state(rep, name, dev.fetch(name, idx), want)
+        assert fetch.compare(rep, "grad", hg) == 0, step
+        if not fin.skip:
+            fast.adam_update(hg, op, om, ov, oh, sc, fin.coef)
+        fetch.compare(rep, "slot", oh)
+        for name, want in (("master", op), ("m", om), ("v", ov)):
+            rep.mismatches[name] = fast.count_unequal(dev.fetch(name), want)
         assert all(x == 0 for x in rep.mismatches.values()), (step, rep.mismatches)
         assert dev.guards_intact()
-        print(f"  step {step}: skip={fin.skip} coef={float(fin.coef):.6g}", flush=True)
+        print(f"  step {step}: skip={fin.skip} coef={float(fin.coef):.6g}, "
+              f"{dev.count} elements compared", flush=True)
         abi.zero_scaler_update(scaler, bool(res.skip))
         o_scale, o_good = oracle.scaler_update(o_scale, o_good, fin.skip)
         o_t += 0 if fin.skip else 1
