@@ -496,9 +496,9 @@ typedef struct zero_unit_buffers {
 
 /*
  * zero_units_prepare: check a host unit table and fill reduce_block and
- * adam_block; also return the workgroup totals.  The caller then copies the
- * table to device memory and passes both copies to the calls below (the
- * device copy must equal the prepared host copy).
+ * adam_block; also return the workgroup totals.  The calls below take the
+ * prepared host table and a device buffer for it, which each call fills with
+ * the table it has just checked before its kernels read it.
  * Errors: ZERO_EINVAL (n_units < 0, NULL pointers, a shard outside
  * 0..ZERO_MAX_SHARD, ld < shard or not a multiple of 8, grid too large),
  * ZERO_EALIGN (alignment as stated in zero_unit_buffers_t).
@@ -515,22 +515,29 @@ size_t zero_units_workspace_bytes(const zero_unit_buffers_t* units, int32_t n_un
  * flat calls' semantics over all units at once: one squared-norm integer, one
  * overflow flag, one clip coefficient and one skip decision for the rank.
  *   world_size  N (1..ZERO_MAX_RANKS): rows per unit
- *   units_host  host copy of the prepared table (checked, not read by kernels)
- *   units_dev   device copy of the same table (read by the kernels)
+ *   units_host  host, the prepared table: checked, then read before the call
+ *               returns
+ *   units_dev   device, n_units * sizeof(zero_unit_buffers_t) bytes, 8-byte
+ *               aligned, caller-owned: the call writes units_host there on
+ *               `stream` (passed by value through a small kernel's
+ *               arguments) ahead of the kernels that read it, so the kernels
+ *               only ever see the table checked on the host; its content on
+ *               entry does not matter
  *   workspace, dev_result, args, stream: as in the flat calls
  * Errors: as the flat calls, plus ZERO_EINVAL when units_host was not
- * prepared.  Nothing is launched when a check fails.
+ * prepared or units_dev is NULL, ZERO_EALIGN for a misaligned units_dev.
+ * Nothing is launched when a check fails.
  */
 int zero_units_reduce_check(int32_t world_size, const zero_unit_buffers_t* units_host,
-                            const zero_unit_buffers_t* units_dev, int32_t n_units,
+                            zero_unit_buffers_t* units_dev, int32_t n_units,
                             const zero_step_args_t* args, void* workspace, size_t ws_bytes,
                             zero_step_result_t* dev_result, hipStream_t stream);
 int zero_units_adam_apply(const zero_unit_buffers_t* units_host,
-                          const zero_unit_buffers_t* units_dev, int32_t n_units,
+                          zero_unit_buffers_t* units_dev, int32_t n_units,
                           const zero_step_args_t* args, const zero_step_result_t* dev_result,
                           hipStream_t stream);
 int zero_units_step(int32_t world_size, const zero_unit_buffers_t* units_host,
-                    const zero_unit_buffers_t* units_dev, int32_t n_units,
+                    zero_unit_buffers_t* units_dev, int32_t n_units,
                     const zero_step_args_t* args, void* workspace, size_t ws_bytes,
                     zero_step_result_t* dev_result, hipStream_t stream);
 
@@ -550,16 +557,18 @@ int zero_units_step(int32_t world_size, const zero_unit_buffers_t* units_host,
  *                          not used
  *   out_host, out_dev      a prepared table with the same shards; its master,
  *                          m, v and param16 are written, its other fields are
- *                          not used
+ *                          not used; out_dev is filled from out_host like
+ *                          units_dev, and the two device buffers must not
+ *                          overlap
  *   world_size, args, workspace, dev_result, stream: as zero_units_step
  * Errors: as zero_units_step, plus ZERO_EINVAL for max_grad_norm > 0, a shard
- * that differs between the tables, and a unit whose out buffers overlap its
- * in buffers or one another.  Nothing is launched when a check fails.
+ * that differs between the tables, a unit whose out buffers overlap its in
+ * buffers or one another, and overlapping device tables.  Nothing is
+ * launched when a check fails.
  */
 int zero_units_step_1pass(int32_t world_size, const zero_unit_buffers_t* units_host,
-                          const zero_unit_buffers_t* units_dev,
-                          const zero_unit_buffers_t* out_host,
-                          const zero_unit_buffers_t* out_dev, int32_t n_units,
+                          zero_unit_buffers_t* units_dev, const zero_unit_buffers_t* out_host,
+                          zero_unit_buffers_t* out_dev, int32_t n_units,
                           const zero_step_args_t* args, void* workspace, size_t ws_bytes,
                           zero_step_result_t* dev_result, hipStream_t stream);
 
@@ -569,13 +578,14 @@ int zero_units_step_1pass(int32_t world_size, const zero_unit_buffers_t* units_h
  * slots: if dev_result->skip, every unit's param16 is rewritten as the fp16
  * cast of its master (round to nearest even); otherwise nothing happens.
  *   units_host, units_dev  the prepared table of the current state (the one
- *                          the pass read), with param16 at the live slots
+ *                          the pass read), with param16 at the live slots;
+ *                          units_dev is filled as in zero_units_step
  *   dev_result             as written by the step's final finalize
  * Errors: ZERO_EINVAL (a table not prepared, NULL pointers, a slot that
  * overlaps its unit's master), ZERO_EALIGN, ZERO_EHIP.
  */
 int zero_units_slot_restore(const zero_unit_buffers_t* units_host,
-                            const zero_unit_buffers_t* units_dev, int32_t n_units,
+                            zero_unit_buffers_t* units_dev, int32_t n_units,
                             const zero_step_result_t* dev_result, hipStream_t stream);
 
 typedef struct zero_scaler {

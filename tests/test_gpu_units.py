@@ -217,3 +217,47 @@ def test_units_workspace_content_does_not_matter():
     torch.cuda.synchronize()
     r = abi.zero_step_result_t.from_buffer_copy(res.cpu().numpy().tobytes())
     assert r.own_q == 0 and r.norm == 0.0 and not r.skip and r.clip_coef == 1.0
+
+
+@pytest.mark.parametrize("one_pass", [False, True])
+def test_units_device_table_is_the_checked_one(one_pass):
+    """Every zero_units_* call writes the host table it checked into the
+    device table buffer before its kernels read it: a stale table left in that
+    buffer (here a well-formed table of another rank's buffers) changes
+    nothing, and the other buffers are never touched."""
+    print(f"[units device table, one_pass={one_pass}]", flush=True)
+    from zero_sharded_optimizer_rank_amd.units import DeviceUnits
+
+    w = synth.TINY_FSDP
+    kw = dict(one_pass=one_pass)
+    a, ref, other = DeviceUnits(w, 1, **kw), DeviceUnits(w, 1, **kw), DeviceUnits(w, 1, **kw)
+    for d in (a, ref, other):
+        d.load_initial_state()
+    before = {n: other.fetch(n).copy() for n in ("master", "m", "v", "slot")}
+
+    def stale(dst, table):
+        raw = bytes(table)[:dst.numel()]
+        dst.copy_(torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(dst.device))
+        torch.cuda.synchronize()
+
+    for step in (1, 2):
+        for d in (a, ref):
+            d.load_contributions(step, w.loss_scale0)
+        args = a.args(step, w.loss_scale0)
+        stale(a.table_dev, other.table)
+        if one_pass:
+            stale(a.table2_dev, other.table2)
+            a.step_1pass(args)
+            ref.step_1pass(args)
+        else:
+            a.step(args)
+            ref.step(args)
+        ra, rr = a.result(), ref.result()
+        assert bytes(ra) == bytes(rr), step
+        if one_pass and not ra.skip:
+            a.adopt()
+            ref.adopt()
+        for name in ("master", "m", "v", "slot") + (() if one_pass else ("grad",)):
+            assert np.array_equal(_bits(a.fetch(name)), _bits(ref.fetch(name))), (step, name)
+        for name, want in before.items():
+            assert np.array_equal(_bits(other.fetch(name)), _bits(want)), (step, name)

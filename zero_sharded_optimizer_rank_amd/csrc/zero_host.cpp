@@ -124,7 +124,6 @@ int check_reduce_inputs(const zero_plan_t* plan, const uint16_t* const* contrib,
   return check_rows(plan, contrib);
 }
 
-
 int check_reduce_ptrs(const zero_plan_t* plan, const uint16_t* const* contrib, float* grad_out,
                       void* workspace, size_t ws_bytes, zero_step_result_t* dev_result) {
   const int rc = check_reduce_inputs(plan, contrib, workspace, ws_bytes, dev_result);
@@ -559,6 +558,22 @@ int units_layout(zero_unit_buffers_t* units, const zero_unit_buffers_t* cunits, 
   return ZERO_OK;
 }
 
+// The kernels read the table from device memory.  Each call writes the table
+// it has just checked into the caller's device table buffer on its own
+// stream, ahead of its kernels, so no kernel can read a table other than the
+// one validated on the host (a stale or mismatched device copy is simply
+// overwritten).  The entries travel by value in the arguments of a small
+// store kernel, so the host table is read before the call returns and no
+// copy engine reads caller memory later.
+int upload_table(zero_unit_buffers_t* units_dev, const zero_unit_buffers_t* units_host,
+                 int32_t n_units, hipStream_t stream) {
+  if (n_units == 0) return ZERO_OK;
+  if (!units_dev) return fail(ZERO_EINVAL, "units_dev is NULL");
+  if (!aligned(units_dev, 8)) return fail(ZERO_EALIGN, "units_dev not 8-byte aligned");
+  return hip_status(zk::launch_store_table(units_host, n_units, units_dev, stream),
+                    "unit table store launch");
+}
+
 }  // namespace
 
 int zero_units_prepare(zero_unit_buffers_t* units, int32_t n_units, int64_t* reduce_blocks_out,
@@ -579,7 +594,7 @@ size_t zero_units_workspace_bytes(const zero_unit_buffers_t* units, int32_t n_un
 }
 
 int zero_units_reduce_check(int32_t world_size, const zero_unit_buffers_t* units_host,
-                            const zero_unit_buffers_t* units_dev, int32_t n_units,
+                            zero_unit_buffers_t* units_dev, int32_t n_units,
                             const zero_step_args_t* args, void* workspace, size_t ws_bytes,
                             zero_step_result_t* dev_result, hipStream_t stream) {
   g_err[0] = 0;
@@ -601,6 +616,8 @@ int zero_units_reduce_check(int32_t world_size, const zero_unit_buffers_t* units
   const zk::FinalizeArgs fa = finalize_args(&pl, args);
   if (b1 == 0)  // no units: Q = 0, nothing overflowed
     return hip_status(zk::launch_finalize_empty(fa, dev_result, stream), "finalize launch");
+  rc = upload_table(units_dev, units_host, n_units, stream);
+  if (rc) return rc;
   rc = hip_status(zk::launch_units_reduce(units_dev, n_units, b1, world_size, (float)fa.inv64,
                                           workspace, stream),
                   "units reduce launch");
@@ -609,11 +626,11 @@ int zero_units_reduce_check(int32_t world_size, const zero_unit_buffers_t* units
                     "finalize launch");
 }
 
-int zero_units_adam_apply(const zero_unit_buffers_t* units_host,
-                          const zero_unit_buffers_t* units_dev, int32_t n_units,
-                          const zero_step_args_t* args, const zero_step_result_t* dev_result,
-                          hipStream_t stream) {
-  g_err[0] = 0;
+// zero_units_adam_apply with or without the table upload (zero_units_step
+// has uploaded it already, ahead of its reduce).
+static int units_adam(const zero_unit_buffers_t* units_host, zero_unit_buffers_t* units_dev,
+                      int32_t n_units, const zero_step_args_t* args,
+                      const zero_step_result_t* dev_result, bool upload, hipStream_t stream) {
   int rc = check_adam_args(args);
   if (rc) return rc;
   int64_t b1 = 0, b2 = 0;
@@ -623,13 +640,25 @@ int zero_units_adam_apply(const zero_unit_buffers_t* units_host,
   if (!dev_result) return fail(ZERO_EINVAL, "dev_result is NULL");
   if (!aligned(dev_result, 8)) return fail(ZERO_EALIGN, "dev_result not 8-byte aligned");
   if (b2 == 0) return ZERO_OK;
+  if (upload) {
+    rc = upload_table(units_dev, units_host, n_units, stream);
+    if (rc) return rc;
+  }
   return hip_status(zk::launch_units_adam(units_dev, n_units, b2, adam_scalars(args), dev_result,
                                           stream),
                     "units adam launch");
 }
 
+int zero_units_adam_apply(const zero_unit_buffers_t* units_host,
+                          zero_unit_buffers_t* units_dev, int32_t n_units,
+                          const zero_step_args_t* args, const zero_step_result_t* dev_result,
+                          hipStream_t stream) {
+  g_err[0] = 0;
+  return units_adam(units_host, units_dev, n_units, args, dev_result, true, stream);
+}
+
 int zero_units_step(int32_t world_size, const zero_unit_buffers_t* units_host,
-                    const zero_unit_buffers_t* units_dev, int32_t n_units,
+                    zero_unit_buffers_t* units_dev, int32_t n_units,
                     const zero_step_args_t* args, void* workspace, size_t ws_bytes,
                     zero_step_result_t* dev_result, hipStream_t stream) {
   g_err[0] = 0;
@@ -638,13 +667,12 @@ int zero_units_step(int32_t world_size, const zero_unit_buffers_t* units_host,
   rc = zero_units_reduce_check(world_size, units_host, units_dev, n_units, args, workspace,
                                ws_bytes, dev_result, stream);
   if (rc) return rc;
-  return zero_units_adam_apply(units_host, units_dev, n_units, args, dev_result, stream);
+  return units_adam(units_host, units_dev, n_units, args, dev_result, false, stream);
 }
 
 int zero_units_step_1pass(int32_t world_size, const zero_unit_buffers_t* units_host,
-                          const zero_unit_buffers_t* units_dev,
-                          const zero_unit_buffers_t* out_host,
-                          const zero_unit_buffers_t* out_dev, int32_t n_units,
+                          zero_unit_buffers_t* units_dev, const zero_unit_buffers_t* out_host,
+                          zero_unit_buffers_t* out_dev, int32_t n_units,
                           const zero_step_args_t* args, void* workspace, size_t ws_bytes,
                           zero_step_result_t* dev_result, hipStream_t stream) {
   g_err[0] = 0;
@@ -689,6 +717,14 @@ int zero_units_step_1pass(int32_t world_size, const zero_unit_buffers_t* units_h
   const zk::FinalizeArgs fa = finalize_args(&pl, args);
   if (b1 == 0)
     return hip_status(zk::launch_finalize_empty(fa, dev_result, stream), "finalize launch");
+  {
+    const size_t tb = (size_t)n_units * sizeof(zero_unit_buffers_t);
+    const uintptr_t a = (uintptr_t)units_dev, b = (uintptr_t)out_dev;
+    if (a < b + tb && b < a + tb) return fail(ZERO_EINVAL, "units_dev and out_dev overlap");
+  }
+  rc = upload_table(units_dev, units_host, n_units, stream);
+  if (!rc) rc = upload_table(out_dev, out_host, n_units, stream);
+  if (rc) return rc;
   rc = hip_status(zk::launch_units_reduce_adam_1pass(units_dev, out_dev, n_units, b1,
                                                      world_size, (float)fa.inv64,
                                                      adam_scalars(args), workspace, stream),
@@ -699,7 +735,7 @@ int zero_units_step_1pass(int32_t world_size, const zero_unit_buffers_t* units_h
 }
 
 int zero_units_slot_restore(const zero_unit_buffers_t* units_host,
-                            const zero_unit_buffers_t* units_dev, int32_t n_units,
+                            zero_unit_buffers_t* units_dev, int32_t n_units,
                             const zero_step_result_t* dev_result, hipStream_t stream) {
   g_err[0] = 0;
   int64_t b1 = 0, b2 = 0;
@@ -716,6 +752,8 @@ int zero_units_slot_restore(const zero_unit_buffers_t* units_host,
       return fail(ZERO_EINVAL, "unit %d: slot overlaps master", u);
   }
   if (max_shard == 0) return ZERO_OK;
+  rc = upload_table(units_dev, units_host, n_units, stream);
+  if (rc) return rc;
   return hip_status(zk::launch_units_slot_restore(units_dev, n_units, max_shard, dev_result,
                                                   stream),
                     "units slot restore launch");

@@ -82,6 +82,9 @@ int launch_adam_bf16(const float* grad, float* master, float* m, float* v, uint1
                      hipStream_t stream);
 
 // Multi-unit forms (zero_units.hip): the unit table lives in device memory.
+// launch_store_table writes a host table there through kernel arguments.
+int launch_store_table(const zero_unit_buffers_t* units_host, int32_t n_units,
+                       zero_unit_buffers_t* units_dev, hipStream_t stream);
 int launch_units_reduce(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
                         int n, float inv32, void* workspace, hipStream_t stream);
 int launch_units_adam(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,

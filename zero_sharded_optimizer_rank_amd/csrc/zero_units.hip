@@ -131,7 +131,38 @@ __global__ __launch_bounds__(kThreads) void k_units_slot_restore(
   }
 }
 
+// The unit table, written by value: kTableChunk entries travel in the kernel
+// arguments (48 * 80 B fits the 4 KiB argument segment) and one workgroup
+// stores them as 8-byte words.
+constexpr int kTableChunk = 48;
+struct TableChunk {
+  zero_unit_buffers_t u[kTableChunk];
+};
+constexpr int kTableWords = (int)(sizeof(zero_unit_buffers_t) / 8);
+static_assert(sizeof(zero_unit_buffers_t) % 8 == 0, "whole 8-byte words");
+
+__global__ __launch_bounds__(kThreads) void k_store_table(TableChunk c, int32_t n,
+                                                           zero_unit_buffers_t* __restrict__ dst) {
+  const uint64_t* src = (const uint64_t*)&c.u[0];
+  uint64_t* out = (uint64_t*)dst;
+  for (int i = threadIdx.x; i < n * kTableWords; i += kThreads) out[i] = src[i];
+}
+
 }  // namespace
+
+int launch_store_table(const zero_unit_buffers_t* units_host, int32_t n_units,
+                       zero_unit_buffers_t* units_dev, hipStream_t stream) {
+  for (int32_t u0 = 0; u0 < n_units; u0 += kTableChunk) {
+    const int32_t n = n_units - u0 < kTableChunk ? n_units - u0 : kTableChunk;
+    TableChunk c;
+    for (int32_t i = 0; i < n; ++i) c.u[i] = units_host[u0 + i];
+    for (int32_t i = n; i < kTableChunk; ++i) c.u[i] = zero_unit_buffers_t{};
+    hipLaunchKernelGGL(k_store_table, dim3(1), dim3(kThreads), 0, stream, c, n, units_dev + u0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  return (int)hipSuccess;
+}
 
 int launch_units_slot_restore(const zero_unit_buffers_t* units_dev, int32_t n_units,
                               int64_t max_shard, const zero_step_result_t* res,

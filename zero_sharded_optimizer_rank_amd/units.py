@@ -131,8 +131,10 @@ class DeviceUnits:
         self._pin32 = torch.empty(CHUNK, dtype=torch.float32, pin_memory=True)
 
     def _to_device(self, table) -> torch.Tensor:
-        raw = bytes(table)[:abi.UNIT_BUFFERS_BYTES * self.n_units] or b"\0"
-        return torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(self.device)
+        """Device memory for a unit table: every zero_units_* call writes the
+        host table it checks there itself, so nothing is copied here."""
+        return torch.empty(max(abi.UNIT_BUFFERS_BYTES * self.n_units, 8), dtype=torch.uint8,
+                           device=self.device)
 
     # ---------------------------------------------------------------- layout
     def unit_real(self, u: int) -> int:
