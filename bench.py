@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCES = ("zero_sharded_optimizer_rank_amd/csrc/zero_kernels.hip",
                   "zero_sharded_optimizer_rank_amd/csrc/zero_units.hip",
+                  "zero_sharded_optimizer_rank_amd/csrc/zero_noalloc.hip",
                   "zero_sharded_optimizer_rank_amd/csrc/zero_device.h",
                   "zero_sharded_optimizer_rank_amd/csrc/zero_internal.h")
 
@@ -189,6 +190,150 @@ def calibration_copy(nbytes: float, stream):
     return {"copy_gbps": best, "bytes": nb}
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries for profiles/: kernel durations from a --kernel-trace
+# --stats run of this script, HBM bytes from two --pmc runs (FETCH_SIZE, then
+# WRITE_SIZE), each scaled by what the same counter reads for the calibration
+# copy of known size in the same run.
+
+PROF_KERNELS = ("k12u_reduce_adam", "k12_reduce_adam_bf16", "k12_reduce_adam", "k1u_reduce_check",
+                "k2u_adam", "k1_reduce_check_bf16", "k2_adam_bf16", "kt_tree_finalize_bf16",
+                "k1_reduce_check", "kf_reduce_finalize", "k2_adam", "k_store_table", "calib_copy")
+
+
+def _prof_short(name: str):
+    for k in PROF_KERNELS:
+        if k + "(" in name or name.endswith(k) or ("::" + k) in name:
+            return k
+    return None
+
+
+def _prof_file(pattern: str, d: str) -> str:
+    import glob
+    f = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+    if not f:
+        raise FileNotFoundError(f"no {pattern} under {d}")
+    return f[0]
+
+
+def _json_line(path: str) -> dict:
+    with open(path) as f:
+        lines = [ln for ln in f if ln.startswith("{")]
+    if not lines:
+        raise ValueError(f"no JSON line in {path}")
+    return json.loads(lines[-1])
+
+
+def summarize_rocprof(label: str, bench_args: str, pmc_args: str, out: str = "gpurun_out",
+                      prof: str = ""):
+    """Write profiles/<kernels>_<label>_{kernel_stats,hbm_traffic}.md and
+    profiles/traffic_<label>.json (or into `prof`) from the rocprofv3 outputs
+    that the commands written into those files leave under `out`."""
+    import csv
+
+    kt_dir = os.path.join(out, f"prof_kt_{label}")
+    kt_log = os.path.join(out, f"bench_kt_{label}.log")
+    j = _json_line(kt_log)
+    S, N = int(j["config"]["shard"]), int(j["config"]["world_size_simulated"])
+    one_pass = "single pass" in j["metric"]
+    desc = j["config"]["workload"]
+
+    def algo(k):
+        if k.startswith("k12"):
+            return (2 * N + 26) * S
+        if k.startswith("k1"):
+            return (2 * N + 4) * S
+        if k.startswith("k2"):
+            return 30 * S
+        return None
+
+    stats = {}
+    for r in csv.DictReader(open(_prof_file("*kernel_stats.csv", kt_dir))):
+        k = _prof_short(r["Name"])
+        if k is not None:
+            stats[k] = dict(calls=int(r["Calls"]), avg=float(r["AverageNs"]) / 1e3,
+                            mn=float(r["MinNs"]) / 1e3, mx=float(r["MaxNs"]) / 1e3)
+
+    def counters(cname):
+        d = os.path.join(out, f"prof_{cname}_{label}")
+        acc = {}
+        for r in csv.DictReader(open(_prof_file("*counter_collection.csv", d))):
+            if r["Counter_Name"] != cname:
+                continue
+            k = _prof_short(r["Kernel_Name"])
+            if k is not None:
+                acc.setdefault(k, []).append(float(r["Counter_Value"]))
+        calib = float(_json_line(os.path.join(out, f"bench_{cname}_{label}.log"))
+                      ["calibration_copy"]["bytes"])
+        return {k: sum(v) / len(v) for k, v in acc.items()}, calib
+
+    fetch, calib_f = counters("FETCH_SIZE")
+    write, calib_w = counters("WRITE_SIZE")
+    fs = calib_f / (fetch["calib_copy"] * 1024)
+    ws = calib_w / (write["calib_copy"] * 1024)
+    kh = kernel_hash()
+    rec = {"kernel_hash": kh, "workload": label, "fetch_scale": fs, "write_scale": ws,
+           "kernels": {}}
+    for k in fetch:
+        if k == "calib_copy":
+            continue
+        rb, wb = fetch[k] * 1024 * fs, write.get(k, 0.0) * 1024 * ws
+        rec["kernels"][k] = {"read_bytes": rb, "write_bytes": wb, "bytes_per_launch": rb + wb,
+                             "algorithmic_bytes": algo(k)}
+    prof = prof or os.path.join(ROOT, "profiles")
+    with open(os.path.join(prof, f"traffic_{label}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+
+    kt_cmd = (f"rocprofv3 --kernel-trace --stats -f csv -d {kt_dir} -o {label} -- "
+              f"python3 bench.py {bench_args} --cpu-procs 1 > {kt_log}")
+    pmc_cmds = [f"timeout -s KILL 300 rocprofv3 --pmc {c} -f csv -d {out}/prof_{c}_{label} "
+                f"-o {label} -- python3 bench.py {pmc_args} > {out}/bench_{c}_{label}.log"
+                for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    sum_cmd = (f"python3 bench.py --summarize-rocprof {label} --bench-args \"{bench_args}\" "
+               f"--pmc-args \"{pmc_args}\"")
+    recipe = ("Commands (from the repository root on one MI355X, with TMPDIR=/tmp; the last "
+              "one reads their output and writes this file):\n\n```\n" + kt_cmd + "\n"
+              + "\n".join(pmc_cmds) + "\n" + sum_cmd + "\n```\n\n")
+    prefix = "k12" if one_pass else "k1_k2"
+    calib_kt = (j.get("calibration_copy") or {}).get("bytes")
+    with open(os.path.join(prof, f"{prefix}_{label}_kernel_stats.md"), "w") as f:
+        f.write(f"# Kernel durations: {desc}\n\n" + recipe +
+                f"Kernel source hash (bench.py `kernel_hash`): `{kh}`.\n\n"
+                "| kernel | calls | avg (us) | min (us) | max (us) | algorithmic bytes / launch "
+                "| GB/s at avg |\n|---|---|---|---|---|---|---|\n")
+        for k, v in sorted(stats.items(), key=lambda kv: -kv[1]["avg"]):
+            a = 2 * calib_kt if (k == "calib_copy" and calib_kt) else algo(k)
+            f.write(f"| {k} | {v['calls']} | {v['avg']:.1f} | {v['mn']:.1f} | {v['mx']:.1f} | "
+                    + (f"{a / 1e9:.3f} GB | {a / (v['avg'] * 1e3):.0f} |" if a else "- | - |")
+                    + "\n")
+        f.write("\nThe JSON line this traced run printed (HIP events on the launch stream):\n\n")
+        for k, v in j["kernels"].items():
+            f.write(f"- {k}: {v['ms'] * 1e3:.1f} us ({v['gbps']:.0f} GB/s)\n")
+        f.write(f"- step {j['ms_per_step'] * 1e3:.1f} us, {j['value'] / 1e9:.2f} G params/s\n")
+        f.write("\nOnly this library's kernels and the calibration copy (`calib_copy`, a one-shot "
+                "copy of known size) are listed; torch's set-up kernels are left out.  "
+                "Algorithmic bytes: 2N + 4 per element for the reduce, 30 for the update, "
+                "2N + 26 for the single pass.\n")
+    with open(os.path.join(prof, f"{prefix}_{label}_hbm_traffic.md"), "w") as f:
+        f.write(f"# HBM traffic per launch: {desc}\n\n" + recipe +
+                f"Kernel source hash: `{kh}`.  Counter values are KiB per dispatch, averaged "
+                "over the dispatches.\n\n"
+                f"Calibration: calib_copy moves exactly {calib_f:.0e} bytes each way per call. "
+                f"FETCH_SIZE reads {fetch['calib_copy']:.1f} KiB for it (scale x{fs:.4f}); "
+                f"WRITE_SIZE reads {write['calib_copy']:.1f} KiB (scale x{ws:.4f}).\n\n"
+                "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes (scaled) | write bytes "
+                "(scaled) | total | algorithmic | total / algorithmic |\n"
+                "|---|---|---|---|---|---|---|---|\n")
+        for k, v in rec["kernels"].items():
+            a = v["algorithmic_bytes"]
+            f.write(f"| {k} | {fetch[k]:.1f} | {write.get(k, 0):.1f} | "
+                    f"{v['read_bytes'] / 1e9:.4f} GB | {v['write_bytes'] / 1e9:.4f} GB | "
+                    f"{v['bytes_per_launch'] / 1e9:.4f} GB | "
+                    + (f"{a / 1e9:.4f} GB | {v['bytes_per_launch'] / a:.4f} |" if a
+                       else "- | - |") + "\n")
+    print(f"wrote profiles for {label}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,7 +371,14 @@ def main():
                          "config; needed for --one-pass on workloads that clip)")
     ap.add_argument("--calib-bytes", type=float, default=4e9,
                     help="bytes of the calibration copy timed next to the step (0: skip)")
+    ap.add_argument("--summarize-rocprof", metavar="LABEL", default=None,
+                    help="no GPU: write profiles/ summaries for LABEL from the rocprofv3 "
+                         "output of the commands they list (with --bench-args, --pmc-args)")
+    ap.add_argument("--bench-args", default="", help="--summarize-rocprof: the traced run's args")
+    ap.add_argument("--pmc-args", default="", help="--summarize-rocprof: the counter runs' args")
     a = ap.parse_args()
+    if a.summarize_rocprof:
+        return summarize_rocprof(a.summarize_rocprof, a.bench_args, a.pmc_args)
     if a.gpus != 1:
         print("bench.py measures the shard step on one GPU only; --gpus must be 1 "
               "(the multi-GPU exchange around the step is not built)", file=sys.stderr)
@@ -253,6 +405,9 @@ def main():
     abi.lib()
     if a.offload:
         return offload_main(a, w)
+    if a.in_place_slot and not a.one_pass:
+        print("--in-place-slot applies to the single pass only (add --one-pass)", file=sys.stderr)
+        sys.exit(2)
     if a.one_pass:
         return one_pass_main(a, w)
     if w.units is not None:
@@ -387,7 +542,7 @@ def one_pass_main(a, w):
     if w.units is not None:
         from zero_sharded_optimizer_rank_amd.units import DeviceUnits
         kname = "k12u_reduce_adam"
-        dev = DeviceUnits(w, a.rank, one_pass=True)
+        dev = DeviceUnits(w, a.rank, one_pass=True, in_place_slot=a.in_place_slot)
         real, S = dev.real_count(), dev.plan.rank_shard
     else:
         kname = "k12_reduce_adam_bf16" if w.dtype == "bf16" else "k12_reduce_adam"
@@ -403,10 +558,13 @@ def one_pass_main(a, w):
     # step must have applied, so adopting each new set unconditionally is right
     res = torch.zeros((a.warmup + a.steps, abi.RESULT_BYTES), dtype=torch.uint8,
                       device=dev.device)
-    in_place = a.in_place_slot and w.units is None
+    in_place = a.in_place_slot
 
     def one_step(t, r):
-        if in_place:
+        if in_place and w.units is not None:  # the unit tables already point at the live slots
+            dev.step_1pass(dev.args(t, w.loss_scale0, other_sq=other_sq), res=r)
+            dev.restore_slot(res=r)
+        elif in_place:
             dev.step_1pass(dev.args(t, w.loss_scale0, other_sq=other_sq), res=r,
                            in_place_slot=True)
             dev.restore_slot(res=r)
