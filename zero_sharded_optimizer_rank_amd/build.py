@@ -68,6 +68,50 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# Sanitizer builds of the host code, for CPU runs only: the C-ABI host
+# sources built by g++ with AddressSanitizer + UndefinedBehaviorSanitizer
+# ("asan") or ThreadSanitizer ("tsan"), linked with the unsanitized kernel
+# objects of build() and with tests/host_sanitize_driver.cpp; "asan" also
+# gives a library that the CPU tests load through ZERO_SHARD_LIB (with the
+# ASan runtime preloaded).  The device code is never built with a sanitizer.
+SAN_FLAGS = {
+    "asan": ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+             "-fno-omit-frame-pointer"],
+    "tsan": ["-fsanitize=thread"],
+}
+
+
+def build_host_sanitized(kind: str) -> dict:
+    flags = SAN_FLAGS[kind]
+    out = os.path.join(BUILD_DIR, f"san_{kind}")
+    os.makedirs(out, exist_ok=True)
+    gxx = ["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-pthread", "-ffp-contract=off",
+           "-fno-math-errno", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-I", INCLUDE,
+           "-I", CSRC, *flags]
+    objs = []
+    for src in ("zero_host.cpp", "zero_offload.cpp"):
+        o = os.path.join(out, src.replace(".cpp", ".o"))
+        _run([*gxx, "-c", os.path.join(CSRC, src), "-o", o])
+        objs.append(o)
+    kobjs = [os.path.join(BUILD_DIR, f) for f in ("zero_kernels.o", "zero_units.o",
+                                                  "zero_noalloc.o")]
+    if not all(os.path.exists(k) for k in kobjs):
+        build()
+    link = ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lamdhip64"]
+    driver = os.path.join(out, "host_sanitize_driver")
+    _run([*gxx, os.path.join(ROOT, "tests", "host_sanitize_driver.cpp"), *objs, *kobjs, *link,
+          "-o", driver])
+    res = {"driver": driver}
+    if kind == "asan":
+        lib = os.path.join(out, "libzero_shard_asan.so")
+        _run([*gxx, "-shared", *objs, *kobjs, *link, "-o", lib])
+        res["lib"] = lib
+    return res
+
+
 if __name__ == "__main__":
-    build()
+    if len(sys.argv) > 1 and sys.argv[1] in SAN_FLAGS:
+        print(build_host_sanitized(sys.argv[1]))
+    else:
+        build()
     sys.exit(0)
