@@ -462,21 +462,34 @@ def main():
 
     skipped = None
     if a.time_skip:
-        # a skipped step (another rank overflowed): the reduce runs, the update exits
-        sk = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        sk_args = dev.args(a.warmup + a.steps + 1, w.loss_scale0, other_sq=other_sq,
-                           other_overflow=True)
-        sk[0].record(stream)
-        for _ in range(3):
-            dev.reduce_check(sk_args)
-            dev.adam_apply(sk_args)
-        sk[1].record(stream)
+        # skipped steps, each as zero_reduce_adam_step (or its unit / bf16 form)
+        # enqueues it: (1) another rank overflowed, known on the host, so the
+        # update is not launched; (2) this rank's own contributions hold an
+        # inf, found on the device, so the update kernel starts and exits
+        def time_skips(other):
+            sk = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            args = dev.args(a.warmup + a.steps + 1, w.loss_scale0, other_sq=other_sq,
+                            other_overflow=other)
+            sk[0].record(stream)
+            for _ in range(3):
+                dev.step(args)
+            sk[1].record(stream)
+            torch.cuda.synchronize()
+            if not dev.result().skip:
+                raise RuntimeError("the forced skip was not taken")
+            return sk[0].elapsed_time(sk[1]) / 3
+
+        other_ms = time_skips(True)
+        row0 = dev.contrib[0] if n_units is None else dev.bufs[0]["contrib"][0]
+        keep = row0[0].item()
+        row0[0] = 0x7F80 if w.dtype == "bf16" else 0x7C00  # +inf in rank 0's first element
         torch.cuda.synchronize()
-        if not dev.result().skip:
-            raise RuntimeError("the forced skip was not taken")
-        skip_ms = sk[0].elapsed_time(sk[1]) / 3
-        skipped = {"ms": skip_ms, "bytes_per_param": 2 * n + 4,
-                   "gbps": (2 * n + 4) * S / (skip_ms * 1e6)}
+        own_ms = time_skips(False)
+        row0[0] = keep
+        torch.cuda.synchronize()
+        skipped = {"other_rank_ms": other_ms, "own_overflow_ms": own_ms,
+                   "bytes_per_param": 2 * n + 4,
+                   "gbps_other_rank": (2 * n + 4) * S / (other_ms * 1e6)}
 
     b1, b2 = bytes_per_param(n)
     kernels = {

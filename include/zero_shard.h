@@ -235,6 +235,8 @@ int zero_adam_apply(const zero_plan_t* plan, int32_t rank, const float* grad, fl
 /*
  * zero_reduce_adam_step: the whole step, zero_reduce_check then
  * zero_adam_apply, enqueued back to back with no host synchronisation.
+ * When args->other_overflow is set the finalize is certain to skip the step,
+ * so the update kernel is not launched (dev_result is as after any skip).
  * Arguments and errors as the two calls; nothing is launched if any argument
  * check fails.
  */
@@ -285,17 +287,28 @@ int zero_reduce_adam_step_noalloc(const zero_plan_t* plan, int32_t rank,
  *   contrib, workspace, ws_bytes, dev_result   as zero_reduce_check
  *   master_in, m_in, v_in     device [S] fp32, 16-byte aligned, read only
  *   master_out, m_out, v_out  device [S] fp32, 16-byte aligned, written
- *   param16_slot_out          device [S] fp16 bit patterns, 2-byte aligned
- *                             (a second flat buffer's slot at rank * S)
+ *   param16_slot_out          device [S] fp16 bit patterns, 2-byte aligned:
+ *                             either a second flat buffer's slot at rank * S,
+ *                             or the live slot itself (see zero_slot_restore)
  *   args                      as zero_reduce_adam_step; max_grad_norm <= 0
  * Results: when dev_result->skip is 0 the out state and slot hold exactly what
  * zero_reduce_adam_step would have left in master, m, v and the slot (the
  * caller adopts them, e.g. by swapping buffer sets); when it is 1 they hold
  * unspecified values and the in state is the unchanged state (the caller
- * keeps it and its slot).  dev_result is bit-identical to zero_reduce_check's
- * with clip_coef 1.  Across ranks, the caller all-reduces own_q and overflow
- * after the pass and calls zero_finalize with the other ranks' values; the
- * skip it writes then decides the adoption on every rank alike.
+ * keeps it; with a second slot buffer, it also keeps the old slot; with the
+ * live slot as param16_slot_out, the slot holds garbage until
+ * zero_slot_restore has run after the step's final finalize, and nothing may
+ * read it before).  dev_result is bit-identical to zero_reduce_check's with
+ * clip_coef 1.  Across ranks, the caller all-reduces own_q and overflow after
+ * the pass and calls zero_finalize with the other ranks' values; the skip it
+ * writes then decides the adoption on every rank alike.
+ * When to use it: it saves the gradient's round trip (8 of 2N + 34 bytes per
+ * element), which pays at small N (Llama-3-8B at N = 8: 6.74 ms against
+ * 7.70 ms on an MI355X).  At N = 64 the contribution rows are 83% of its bytes
+ * and its mixed stream of 67 inputs and 4 outputs runs about 8% below the
+ * reduce's rate, so the two-pass step is as fast or faster there (GPT-2
+ * shard 0.641 against 0.649 ms, flat 7.5B shard 3.00 against 3.15 ms): use
+ * zero_reduce_adam_step above N = 8.
  * Errors: as zero_reduce_adam_step, plus ZERO_EINVAL for max_grad_norm > 0,
  * for an out buffer that overlaps an in buffer, and for out buffers that
  * overlap one another.  Nothing is launched if a check fails.
@@ -551,7 +564,9 @@ int zero_units_step(int32_t world_size, const zero_unit_buffers_t* units_host,
  * coefficient 1).  When dev_result->skip is 0 the out buffers hold exactly
  * what zero_units_step would have left in the current ones (the caller swaps
  * the tables); when it is 1 they hold unspecified values and the current
- * state is unchanged.
+ * state is unchanged.  The out table's param16 may point at the live unit
+ * slots; then, after a skip, they hold garbage until zero_units_slot_restore
+ * has run after the step's final finalize, and nothing may read them before.
  *   units_host, units_dev  the prepared table of the current state: rows
  *                          (contrib, ld) and master, m, v are read; grad is
  *                          not used

@@ -157,3 +157,57 @@ def test_onepass_in_place_slot_graph_replays_match_eager():
         for k in got:
             assert np.array_equal(got[k].view(np.uint8), eager[i][k].view(np.uint8)), (i, k)
         assert dg.guards_intact()
+
+
+def test_onepass_in_place_slot_skipped_step_graph():
+    """A skipped single pass that wrote the live slot, captured with its
+    zero_slot_restore: every replay leaves the state untouched and the slot
+    recast from the unchanged master, the same bits as the eager calls (the
+    restore's rewrite branch runs from the graph)."""
+    from zero_sharded_optimizer_rank_amd.shard import DeviceShard
+
+    w = synth.GPT2
+    rank, begin, count = 1, 777, 200_003
+    print("[graph one pass in place, skipped step]", flush=True)
+    s_eager, s_graph = torch.cuda.Stream(), torch.cuda.Stream()
+    de = DeviceShard(w, rank, begin, count, stream=s_eager, one_pass=True)
+    dg = DeviceShard(w, rank, begin, count, stream=s_graph, one_pass=True)
+    for d in (de, dg):
+        d.load_initial_state()
+        d.load_contributions(1, w.loss_scale0)
+    args = de.args(1, w.loss_scale0, other_overflow=True)  # another rank overflowed
+
+    def skipped_step(d):  # never adopted: the step is skipped
+        d.step_1pass(args, in_place_slot=True)
+        d.restore_slot()
+
+    def snap(d):
+        d.stream.synchronize()
+        out = {x: d.fetch(x).copy() for x in ("master", "m", "v", "slot")}
+        out["res"] = d.res.cpu().numpy().copy()
+        return out
+
+    start = snap(de)
+    eager = []
+    for _ in range(3):
+        skipped_step(de)
+        eager.append(snap(de))
+        assert de.result().skip
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=s_graph):
+        skipped_step(dg)
+    torch.cuda.synchronize()
+    for i in range(3):
+        dg.slot.fill_(0x1234)  # the restore must rewrite every element
+        graph.replay()
+        torch.cuda.synchronize()
+        got = snap(dg)
+        junk = torch.randn(1 << 20, device="cuda").sum().item()
+        assert np.isfinite(junk)
+        for k in got:
+            assert np.array_equal(got[k].view(np.uint8), eager[i][k].view(np.uint8)), (i, k)
+        for k in ("master", "m", "v", "slot"):
+            assert np.array_equal(got[k].view(np.uint8), start[k].view(np.uint8)), (i, k)
+        assert np.array_equal(got["slot"], got["master"].astype(np.float16).view(np.uint16))
+        assert dg.result().skip and dg.guards_intact()

@@ -261,3 +261,28 @@ def test_units_device_table_is_the_checked_one(one_pass):
             assert np.array_equal(_bits(a.fetch(name)), _bits(ref.fetch(name))), (step, name)
         for name, want in before.items():
             assert np.array_equal(_bits(other.fetch(name)), _bits(want)), (step, name)
+
+
+def test_units_step_other_overflow_launches_no_update():
+    """zero_units_step with another rank's overflow: the skip is certain, the
+    update is not launched, the result word says skip and the state, slots
+    and g of every unit match a phase-split step that ran the update kernel."""
+    print("[units step with other_overflow]", flush=True)
+    from zero_sharded_optimizer_rank_amd.units import DeviceUnits
+
+    w = synth.TINY_FSDP
+    a, b = DeviceUnits(w, 3), DeviceUnits(w, 3)
+    for d in (a, b):
+        d.load_initial_state()
+        d.load_contributions(1, w.loss_scale0)
+    before = {n: a.fetch(n).copy() for n in ("master", "m", "v", "slot")}
+    args = a.args(1, w.loss_scale0, other_overflow=True)
+    a.step(args)
+    b.reduce_check(args)
+    b.adam_apply(args)
+    ra, rb = a.result(), b.result()
+    assert ra.skip and bytes(ra) == bytes(rb)
+    for name, want in before.items():
+        assert np.array_equal(_bits(a.fetch(name)), _bits(want)), name
+        assert np.array_equal(_bits(b.fetch(name)), _bits(want)), name
+    assert np.array_equal(_bits(a.fetch("grad")), _bits(b.fetch("grad")))

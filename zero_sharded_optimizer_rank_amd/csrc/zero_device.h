@@ -57,23 +57,30 @@
 // one-wave workgroups a CU holds: 160 KiB / 14848 B = 11.  With the default
 // 32 waves per CU the eight streams of the update thrash the memory system;
 // measured on the Llama-3-8B shard: 32 waves 5.90 TB/s, 16 waves 6.35,
-// 12 waves 6.44, 11 waves 6.53, 10 waves 6.43, 8 waves 6.21.  (The reduce
-// kernel runs best uncapped.)
+// 12 waves 6.44, 11 waves 6.53, 10 waves 6.43, 8 waves 6.21.  Other shapes,
+// interleaved with this one on the same shard (6.55-6.57 TB/s): two quads per
+// thread at 6 / 8 / 11 / 14 workgroups per CU 5.64 / 6.42 / 6.07 / 5.77;
+// two-wave workgroups at 5 / 6 / 7 per CU 5.94 / 6.27 / 6.12; one quad at
+// 9 / 10 / 12 per CU 6.18 / 6.45 / 6.48.
 #ifndef ZK_K2_LDS
 #define ZK_K2_LDS 14848
 #endif
 // The reduce kernel is capped the same way, by N: with 128-thread (two-wave)
-// workgroups, 16 per CU for N <= 8 and 12 per CU beyond (10240 and 13312 B
+// workgroups, 16 per CU for N <= 8 and 10 per CU beyond (10240 and 16384 B
 // of reserved LDS).  Measured reduce rates, cap 10 / 12 / 14 / 16 / none:
 // N = 8:  5.65 / 6.24 / 6.51 / 6.51 / 6.05 TB/s;  N = 16: 6.21 / 6.39 /
 // 6.21 / 6.20 / 6.09;  N = 32: 6.20 / 6.22 / 6.03 / 6.01 / 5.93;  N = 64:
 // 6.26 / 6.20 / 5.99 / 6.00 / 5.94 (the earlier 512-thread, 8-row-batch
-// form: 6.23, 5.66, 5.56, 5.77).
+// form: 6.23, 5.66, 5.56, 5.77).  A finer interleaved sweep at N = 64, caps
+// 9 / 10 / 11 / 12 / 13 / 14 / 16: flat 7.5B shard 6.12 / 6.26 / 6.27 / 6.23
+// / 6.14 / 5.99 / 5.99 TB/s, GPT-2 shard 6.09 / 6.17 / 6.15 / 6.09 / 6.05 /
+// 5.94 / 5.92; at N = 8, caps 13 / 14 / 16 / 18 / 20: 6.37 / 6.50 / 6.50 /
+// 6.05 / 6.05.
 #ifndef ZK_K1_LDS_SMALL_N
 #define ZK_K1_LDS_SMALL_N 10240
 #endif
 #ifndef ZK_K1_LDS
-#define ZK_K1_LDS 13312
+#define ZK_K1_LDS 16384
 #endif
 // The single-pass kernel (reduce and update in one pass, steps without
 // clipping) streams N + 3 inputs and 4 outputs.  One-wave workgroups, 16 per

@@ -291,7 +291,9 @@ int zero_reduce_adam_step(const zero_plan_t* plan, int32_t rank, const uint16_t*
   if (rc) return rc;
   rc = zero_reduce_check(plan, rank, contrib, args, grad_out, workspace, ws_bytes, dev_result,
                          stream);
-  if (rc) return rc;
+  // another rank's overflow makes the finalize skip the step: the update
+  // kernel would only start and exit, so it is not launched
+  if (rc || args->other_overflow) return rc;
   return zero_adam_apply(plan, rank, grad_out, master, m, v, param16_slot, args, dev_result,
                          stream);
 }
@@ -470,7 +472,7 @@ int zero_reduce_adam_step_bf16(const zero_plan_t* plan, int32_t rank,
   if (rc) return rc;
   rc = zero_reduce_check_bf16(plan, rank, contrib, args, grad_out, workspace, ws_bytes, dev_result,
                               stream);
-  if (rc) return rc;
+  if (rc || args->other_overflow) return rc;  // a certain skip: no update launch
   return zero_adam_apply_bf16(plan, rank, grad_out, master, m, v, param_bf16_slot, args,
                               dev_result, stream);
 }
@@ -666,7 +668,7 @@ int zero_units_step(int32_t world_size, const zero_unit_buffers_t* units_host,
   if (rc) return rc;
   rc = zero_units_reduce_check(world_size, units_host, units_dev, n_units, args, workspace,
                                ws_bytes, dev_result, stream);
-  if (rc) return rc;
+  if (rc || args->other_overflow) return rc;  // a certain skip: no update launch
   return units_adam(units_host, units_dev, n_units, args, dev_result, false, stream);
 }
 

@@ -95,7 +95,8 @@ extern "C" int zero_reduce_adam_step_noalloc(const zero_plan_t* plan, int32_t ra
   rc = hip_status(zk::launch_reduce_check(contrib, (int)plan->world_size, plan->shard,
                                           (float)fa.inv64, grad_out, ws, fa, dev_result, stream),
                   "reduce_check launch");
-  if (rc || plan->shard == 0) return rc;
+  // another rank's overflow makes the finalize skip the step: no update launch
+  if (rc || plan->shard == 0 || args->other_overflow) return rc;
   return hip_status(zk::launch_adam(grad_out, master, m, v, param16_slot, plan->shard,
                                     adam_scalars(args), dev_result, stream),
                     "adam launch");
