@@ -19,7 +19,9 @@
  *   - Device calls are asynchronous on the given HIP stream; results in
  *     device memory are readable once the caller synchronises that stream.
  *   - The library allocates no memory.  Every buffer is owned by the caller
- *     and must stay alive until the stream has passed the call.
+ *     and must stay alive until the stream has passed the call.  The only
+ *     device memory the library holds is the fixed scratch array of
+ *     zero_reduce_adam_step_noalloc, a variable of its loaded code object.
  *   - Pointers marked "device" are HIP device pointers; "host" are host
  *     pointers read before the call returns.
  *   - A workspace or result buffer used by one call must not be used by an

@@ -211,3 +211,52 @@ def test_onepass_in_place_slot_skipped_step_graph():
             assert np.array_equal(got[k].view(np.uint8), start[k].view(np.uint8)), (i, k)
         assert np.array_equal(got["slot"], got["master"].astype(np.float16).view(np.uint16))
         assert dg.result().skip and dg.guards_intact()
+
+
+def test_noalloc_step_graph_replays_match_step_with_workspace():
+    """zero_reduce_adam_step_noalloc captured in a HIP graph (its scratch
+    address resolved by one earlier call on the device): three replays give
+    the bits of three eager zero_reduce_adam_step calls with a workspace."""
+    from zero_sharded_optimizer_rank_amd import abi
+    from zero_sharded_optimizer_rank_amd.shard import DeviceShard
+
+    w = synth.LLAMA3_8B
+    p = orun.workload_plan(w)
+    rank, begin, count = 1, 333, 200_003
+    other_sq = w.other_sq(p.real(rank))
+    print("[graph noalloc]", flush=True)
+    warm = DeviceShard(synth.TINY, 0, 0, 1000)  # first call on the device: resolves the scratch
+    warm.load_initial_state()
+    warm.load_contributions(1, synth.TINY.loss_scale0)
+
+    def noalloc(d, args):
+        abi.zero_reduce_adam_step_noalloc(d.plan, d.rank, d.contrib_ptrs(), d.master, d.m, d.v,
+                                          d.slot_ptr(), d.grad, args, d.res, d.stream)
+
+    noalloc(warm, warm.args(1, synth.TINY.loss_scale0))
+    torch.cuda.synchronize()
+    s_eager, s_graph = torch.cuda.Stream(), torch.cuda.Stream()
+    de = DeviceShard(w, rank, begin, count, stream=s_eager)
+    dg = DeviceShard(w, rank, begin, count, stream=s_graph)
+    for d in (de, dg):
+        d.load_initial_state()
+        d.load_contributions(1, w.loss_scale0)
+    args = de.args(1, w.loss_scale0, other_sq=other_sq)
+    eager = []
+    for _ in range(3):
+        de.step(args)
+        eager.append(_snapshot(de))
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=s_graph):
+        noalloc(dg, args)
+    torch.cuda.synchronize()
+    for i in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        got = _snapshot(dg)
+        junk = torch.randn(1 << 20, device="cuda").sum().item()
+        assert np.isfinite(junk)
+        for k in got:
+            assert np.array_equal(got[k].view(np.uint8), eager[i][k].view(np.uint8)), (i, k)
+        assert dg.guards_intact()
