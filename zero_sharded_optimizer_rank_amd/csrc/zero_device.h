@@ -82,6 +82,31 @@
 #ifndef ZK_K1_LDS
 #define ZK_K1_LDS 16384
 #endif
+// Above N = 8, on shards of up to ZK_K1_DEFER_MAX_SHARD elements, the reduce
+// defers its gradient stores: each workgroup sums ZK_K1_DEFER consecutive
+// 512-element chunks one after the other, holding the chunks' g quads in
+// registers, and stores them all at the end.  With 64 rows the rows are 97%
+// of the bytes, and the small g stream spread evenly among them slows the
+// reads far more than its own size: on the flat 7.5B shard's geometry,
+// reading the 64 rows alone took 2.12 ms, with the g stores after every
+// chunk 2.46-2.48 ms, with 8 or 16 chunks' stores deferred 2.35 and 2.30 ms
+// (no-arithmetic probes, 8 workgroups per CU); 8 chunks per workgroup without
+// the deferral ran at 2.71 ms.  The built kernel (8 chunks, 9 workgroups per
+// CU) against the one-chunk form at N = 64, interleaved on the same buffers:
+// S = 24 M (GPT-2) 0.480 / 0.524 ms, 60 M 1.228 / 1.269, 117 M (flat 7.5B)
+// 2.415 / 2.466; but S = 250 M 5.63 / 5.38, 500 M 11.46 / 10.66 and 1.08 G
+// (Llama-2-70B) 24.4 / 23.3 ms, so larger shards keep one chunk per
+// workgroup.  At N = 16 and 32 the deferral did not help in the probes, so
+// N <= 8 and the unit reduce keep one chunk per workgroup too.
+#ifndef ZK_K1_DEFER
+#define ZK_K1_DEFER 8
+#endif
+#ifndef ZK_K1_DEFER_LDS
+#define ZK_K1_DEFER_LDS 18176
+#endif
+#ifndef ZK_K1_DEFER_MAX_SHARD
+#define ZK_K1_DEFER_MAX_SHARD ((int64_t)1 << 27)
+#endif
 // The single-pass kernel (reduce and update in one pass, steps without
 // clipping) streams N + 3 inputs and 4 outputs.  One-wave workgroups, 16 per
 // CU for N <= 8 and 20 beyond (10240 and 8192 B of reserved LDS).  Measured
@@ -383,6 +408,46 @@ __device__ inline Partial reduce_block(const Rows& rows, int32_t n, int64_t shar
   const int64_t rel = full - q_first;
   if (rel >= 0 && rel < (int64_t)ZK_K1_THREADS * ZK_K1_QUADS &&
       (int64_t)threadIdx.x == rel % ZK_K1_THREADS)
+    reduce_tail(rows, n, full * 4, shard, inv32, grad, qlo, qhi, bad);
+  block_reduce<ZK_K1_THREADS>(qlo, qhi, bad);
+  return make_partial(qlo, qhi, bad);
+}
+
+// The deferred form of reduce_block: the workgroup covers K chunks of
+// ZK_K1_THREADS quads, [q_first, q_first + K*T); thread t sums its quad of
+// chunk k (q_first + k*T + t) in the same rank order and keeps its g quad in
+// registers until every chunk is summed, then stores them.  The values and
+// the partial are those of K reduce_block workgroups.
+template <int K, typename Rows>
+__device__ inline Partial reduce_block_deferred(const Rows& rows, int32_t n, int64_t shard,
+                                                int64_t q_first, float inv32,
+                                                float* __restrict__ grad) {
+  uint64_t qlo = 0, qhi = 0;
+  uint32_t bad = 0;
+  const int64_t full = shard >> 2;
+  f32x4 g[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t qd = q_first + (int64_t)k * ZK_K1_THREADS + threadIdx.x;
+    if (qd < full) {
+      float acc[4];
+      sum_rows_quad(rows, n, qd * 4, acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        g[k][e] = acc[e] * inv32;
+        uint64_t lo, hi;
+        sq_units(acc[e], lo, hi, bad);
+        add128(qlo, qhi, lo, hi);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t qd = q_first + (int64_t)k * ZK_K1_THREADS + threadIdx.x;
+    if (qd < full) vstore<ZK_K1_NT_STORE>(g[k], (f32x4*)(grad + qd * 4));
+  }
+  const int64_t rel = full - q_first;  // the thread that would own quad `full`: the tail
+  if (rel >= 0 && rel < (int64_t)ZK_K1_THREADS * K && (int64_t)threadIdx.x == rel % ZK_K1_THREADS)
     reduce_tail(rows, n, full * 4, shard, inv32, grad, qlo, qhi, bad);
   block_reduce<ZK_K1_THREADS>(qlo, qhi, bad);
   return make_partial(qlo, qhi, bad);

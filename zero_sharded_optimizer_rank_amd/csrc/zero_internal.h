@@ -34,6 +34,7 @@ struct AdamScalars {
 // the reduce needs: ticket, kFinBlocks second-level partials, one partial per
 // reduce workgroup.
 int64_t k1_blocks(int64_t shard);
+int64_t k1_blocks_deferred(int64_t shard);  // the reduce's deferred form (fewer, deeper workgroups)
 int64_t k2_blocks(int64_t shard);
 size_t workspace_bytes_for_blocks(int64_t reduce_blocks);
 size_t workspace_bytes(int64_t shard);

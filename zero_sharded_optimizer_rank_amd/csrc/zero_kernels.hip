@@ -48,6 +48,18 @@ __global__ __launch_bounds__(ZK_K1_THREADS) void k1_reduce_check(ContribTable ct
   if (threadIdx.x == 0) partials[blockIdx.x] = pt;
 }
 
+// K1 above N = 8 on shards up to ZK_K1_DEFER_MAX_SHARD: each workgroup covers
+// ZK_K1_DEFER chunks and stores their gradients together at the end (see
+// reduce_block_deferred).
+__global__ __launch_bounds__(ZK_K1_THREADS) void k1_reduce_check_deferred(
+    ContribTable ct, int32_t n, int64_t shard, float inv32, float* __restrict__ grad,
+    Partial* __restrict__ partials, uint32_t* __restrict__ ticket) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
+  const int64_t q_first = (int64_t)blockIdx.x * ZK_K1_THREADS * ZK_K1_DEFER;
+  const Partial pt = reduce_block_deferred<ZK_K1_DEFER>(ct, n, shard, q_first, inv32, grad);
+  if (threadIdx.x == 0) partials[blockIdx.x] = pt;
+}
+
 __global__ __launch_bounds__(kThreads) void kf_reduce_finalize(
     const Partial* __restrict__ partials, int64_t n_partials, Partial* __restrict__ level2,
     uint32_t* __restrict__ ticket, FinalizeArgs fa, zero_step_result_t* __restrict__ res) {
@@ -180,6 +192,13 @@ int64_t k1_blocks(int64_t shard) {
   return b < 1 ? 1 : b;
 }
 
+int64_t k1_blocks_deferred(int64_t shard) {
+  const int64_t units = (shard + 3) >> 2;  // quads, the ragged one included
+  const int64_t per = (int64_t)ZK_K1_THREADS * ZK_K1_DEFER;
+  const int64_t b = (units + per - 1) / per;
+  return b < 1 ? 1 : b;
+}
+
 int64_t k12_blocks(int64_t shard) {  // one quad per thread
   const int64_t quads = (shard + 3) >> 2;
   const int64_t b = (quads + ZK_K12_THREADS - 1) / ZK_K12_THREADS;
@@ -227,10 +246,16 @@ int launch_reduce_check(const uint16_t* const* contrib, int n, int64_t shard, fl
                         zero_step_result_t* res, hipStream_t stream) {
   ContribTable ct;
   for (int r = 0; r < ZERO_MAX_RANKS; ++r) ct.p[r] = r < n ? contrib[r] : nullptr;
-  const int64_t blocks = k1_blocks(shard);
-  hipLaunchKernelGGL(k1_reduce_check, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), k1_lds(n), stream, ct,
-                     n, shard, inv32, grad, (Partial*)workspace_partials(workspace),
-                     (uint32_t*)workspace);
+  const bool deferred = n > 8 && shard <= ZK_K1_DEFER_MAX_SHARD;
+  const int64_t blocks = deferred ? k1_blocks_deferred(shard) : k1_blocks(shard);
+  if (deferred)
+    hipLaunchKernelGGL(k1_reduce_check_deferred, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS),
+                       ZK_K1_DEFER_LDS, stream, ct, n, shard, inv32, grad,
+                       (Partial*)workspace_partials(workspace), (uint32_t*)workspace);
+  else
+    hipLaunchKernelGGL(k1_reduce_check, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), k1_lds(n),
+                       stream, ct, n, shard, inv32, grad, (Partial*)workspace_partials(workspace),
+                       (uint32_t*)workspace);
   const int e = (int)hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_partials_finalize(workspace, blocks, fa, res, stream);
