@@ -10,6 +10,7 @@ present.  Every step of every case must match the oracle bit for bit, as in
 the hand-picked parity cases.
 """
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -22,8 +23,11 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-N_CASES = 48
-N_UNIT_CASES = 16
+# ZERO_RANDOM_SCALE=k sets the multiplier of every case count below (default 4;
+# larger values run an extended campaign)
+SCALE = max(1, int(os.environ.get("ZERO_RANDOM_SCALE", "4")))
+N_CASES = 48 * SCALE
+N_UNIT_CASES = 16 * SCALE
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -128,7 +132,7 @@ def test_random_unit_layout_matches_oracle(seed):
     run_units_all_ranks(w)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(12 * SCALE))
 def test_random_configuration_offload_matches_oracle(seed):
     """The offload form (reduce on the GPU, Adam on the host, fp16 back over
     PCIe) on random fp16 configurations, with a random pipeline chunk and
@@ -147,7 +151,7 @@ def test_random_configuration_offload_matches_oracle(seed):
         run_window(w, rank, 0, p.shard, offload=dict(chunk=chunk, threads=threads))
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(16 * SCALE))
 def test_random_configuration_onepass_matches_oracle(seed):
     """The single-pass step on random fp16 and bf16 configurations with
     clipping off, whole shards or windows, injected overflow included."""
@@ -167,7 +171,7 @@ def test_random_configuration_onepass_matches_oracle(seed):
         run_window(w, rank, begin, count, one_pass=True)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(8 * SCALE))
 def test_random_unit_layout_one_pass_matches_oracle(seed):
     """The unit single pass on random unit layouts with clipping off."""
     w = dataclasses.replace(random_unit_workload(100 + seed), max_grad_norm=0.0)
