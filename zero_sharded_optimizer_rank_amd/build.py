@@ -65,7 +65,24 @@ def build(verbose: bool = True) -> str:
     _run([HIPCC, "-x", "hip", *COMMON, *DEVICE_FLAGS, "-shared",
           os.path.join(CSRC, "calib.hip"), "-o", tmp])
     os.replace(tmp, CALIB_LIB)
+    build_c_example()
     return LIB
+
+
+# A plain C program that runs the step through the C ABI with its own
+# hipMalloc buffers (tests/c_abi_step.c, used by tests/test_gpu_c_abi.py).
+C_EXAMPLE = os.path.join(BUILD_DIR, "c_abi_step")
+
+
+def build_c_example() -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    tmp = C_EXAMPLE + ".tmp"
+    _run(["gcc", "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+          "-I", INCLUDE, os.path.join(ROOT, "tests", "c_abi_step.c"), "-L", HERE, "-lzero_shard",
+          "-L/opt/rocm/lib", "-lamdhip64", f"-Wl,-rpath,{HERE}", "-Wl,-rpath,/opt/rocm/lib",
+          "-o", tmp])
+    os.replace(tmp, C_EXAMPLE)
+    return C_EXAMPLE
 
 
 # Sanitizer builds of the host code, for CPU runs only: the C-ABI host
