@@ -45,6 +45,29 @@ def test_tiny_fsdp_all_ranks(variant):
         assert [r.skip for r in reports] == [s == 2 for s in range(1, w.steps + 1)]
 
 
+@pytest.mark.parametrize("variant", ["config", "clipped", "skip"])
+def test_units_deferred_reduce_all_ranks(variant):
+    """Above N = 8 the unit reduce sums eight one-chunk workgroups' worth of
+    quads per workgroup, and a workgroup's chunks may belong to different
+    units.  Sixteen ranks of a layout that mixes units of one element per rank
+    with units of 20 and 5 chunks, so that workgroups start and end inside
+    units and span several small ones; three steps, every rank bit for bit."""
+    print(f"[units deferred reduce N=16 {variant}]", flush=True)
+    w = dataclasses.replace(
+        synth.TINY_FSDP, name="units_n16", cfg_id=16, world_size=16,
+        tensors=(("a", (1000, 37)), ("b", (5,)), ("c", (4,)), ("f", (4096, 40)),
+                 ("d", (300, 7)), ("e", (2,))),
+        units=(0, 1, 2, 3, 4, 5), parity_ranks=tuple(range(16)))
+    max_norm = 0.05 if variant == "clipped" else w.max_grad_norm
+    if variant == "skip":
+        w = dataclasses.replace(w, inject_step=2)
+    reports = run_units_all_ranks(w, max_norm)
+    if variant == "clipped":
+        assert all(r.coef < 1 for r in reports)
+    if variant == "skip":
+        assert [r.skip for r in reports] == [s == 2 for s in range(1, w.steps + 1)]
+
+
 def _feed_units_and_reduce(dev, step, scale, pos):
     """Generate each unit's contributions chunk by chunk, copy them to the
     unit's rows and reduce the same host chunks with the C oracle.  Returns

@@ -97,7 +97,11 @@
 // 2.415 / 2.466; but S = 250 M 5.63 / 5.38, 500 M 11.46 / 10.66 and 1.08 G
 // (Llama-2-70B) 24.4 / 23.3 ms, so larger shards keep one chunk per
 // workgroup.  At N = 16 and 32 the deferral did not help in the probes, so
-// N <= 8 and the unit reduce keep one chunk per workgroup too.
+// N <= 8 keeps one chunk per workgroup too.  The unit reduce defers under
+// the same rule on the units' total: GPT-2 in 50 units at N = 64, 0.514
+// against 0.527 ms (8 chunks at 8 / 10 / 12 per CU 0.554 / 0.525 / 0.554,
+// 16 chunks at 8 / 9 per CU 0.566 / 0.581, 4 chunks at 10 / 12 per CU 0.535
+// / 0.542).
 #ifndef ZK_K1_DEFER
 #define ZK_K1_DEFER 8
 #endif

@@ -74,6 +74,63 @@ __global__ __launch_bounds__(ZK_K1_THREADS) void k1u_reduce_check(
   if (threadIdx.x == 0) partials[b] = pt;
 }
 
+// The deferred form above N = 8 (see reduce_block_deferred): workgroup b
+// takes the ZK_K1_DEFER consecutive workgroups bK .. bK + K - 1 of the
+// one-chunk numbering that zero_units_prepare recorded, so its chunks may lie
+// in different units.  Each chunk's g quad stays in registers until every
+// chunk is summed; the chunk's g address and its count of whole-quad threads
+// are workgroup-uniform.  Each unit's ragged tail is summed and stored where
+// it is met.  The values and the norm are those of the one-chunk kernel; the
+// partials are fewer (one per workgroup).
+static_assert(ZK_K1_QUADS == 1, "a chunk is one one-quad workgroup");
+__global__ __launch_bounds__(ZK_K1_THREADS) void k1u_reduce_check_deferred(
+    const zero_unit_buffers_t* __restrict__ units, int32_t n_units, int64_t chunks, int32_t n,
+    float inv32, Partial* __restrict__ partials, uint32_t* __restrict__ ticket) {
+  constexpr int K = ZK_K1_DEFER;
+  const int64_t b = blockIdx.x;
+  if (b == 0 && threadIdx.x == 0) *ticket = 0u;
+  uint64_t qlo = 0, qhi = 0;
+  uint32_t bad = 0;
+  f32x4 g[K];
+  float* gbase[K];  // the chunk's first quad in its unit's g
+  int32_t whole[K];  // threads of the chunk that own a whole quad
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t c = b * K + k;
+    whole[k] = 0;
+    gbase[k] = nullptr;
+    if (c < chunks) {
+      const int32_t u = find_unit(n_units, c, [&](int32_t i) { return units[i].reduce_block; });
+      const UnitBuffersGlobal& ub = ((const UnitBuffersGlobal*)units)[u];
+      const StridedRows rows{(const uint16_t*)ub.contrib, ub.ld};
+      const int64_t q_first = (c - ub.reduce_block) * ZK_K1_THREADS;
+      const int64_t full = ub.shard >> 2, rel = full - q_first;
+      whole[k] = rel <= 0 ? 0 : rel >= ZK_K1_THREADS ? ZK_K1_THREADS : (int32_t)rel;
+      gbase[k] = (float*)ub.grad + q_first * 4;
+      if ((int32_t)threadIdx.x < whole[k]) {
+        float acc[4];
+        sum_rows_quad(rows, n, (q_first + threadIdx.x) * 4, acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          g[k][e] = acc[e] * inv32;
+          uint64_t lo, hi;
+          sq_units(acc[e], lo, hi, bad);
+          add128(qlo, qhi, lo, hi);
+        }
+      }
+      // the thread that would own quad `full` takes the unit's ragged tail
+      if (rel >= 0 && rel < ZK_K1_THREADS && (int64_t)threadIdx.x == rel)
+        reduce_tail(rows, n, full * 4, ub.shard, inv32, (float*)ub.grad, qlo, qhi, bad);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+    if ((int32_t)threadIdx.x < whole[k])
+      vstore<ZK_K1_NT_STORE>(g[k], (f32x4*)(gbase[k] + threadIdx.x * 4));
+  block_reduce<ZK_K1_THREADS>(qlo, qhi, bad);
+  if (threadIdx.x == 0) partials[b] = make_partial(qlo, qhi, bad);
+}
+
 __global__ __launch_bounds__(ZK_K2_THREADS) void k2u_adam(
     const zero_unit_buffers_t* __restrict__ units, int32_t n_units, AdamScalars sc,
     const zero_step_result_t* __restrict__ res) {
@@ -186,10 +243,20 @@ int launch_units_reduce_adam_1pass(const zero_unit_buffers_t* units_dev,
 }
 
 int launch_units_reduce(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
-                        int n, float inv32, void* workspace, hipStream_t stream) {
-  hipLaunchKernelGGL(k1u_reduce_check, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), k1_lds(n), stream,
-                     units_dev, n_units, n, inv32, (Partial*)workspace_partials(workspace),
-                     (uint32_t*)workspace);
+                        int64_t elems, int n, float inv32, void* workspace, int64_t* n_partials,
+                        hipStream_t stream) {
+  Partial* partials = (Partial*)workspace_partials(workspace);
+  if (n > 8 && elems <= ZK_K1_DEFER_MAX_SHARD) {
+    const int64_t wg = (blocks + ZK_K1_DEFER - 1) / ZK_K1_DEFER;
+    hipLaunchKernelGGL(k1u_reduce_check_deferred, dim3((uint32_t)wg), dim3(ZK_K1_THREADS),
+                       ZK_K1_DEFER_LDS, stream, units_dev, n_units, blocks, n, inv32, partials,
+                       (uint32_t*)workspace);
+    *n_partials = wg;
+  } else {
+    hipLaunchKernelGGL(k1u_reduce_check, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), k1_lds(n),
+                       stream, units_dev, n_units, n, inv32, partials, (uint32_t*)workspace);
+    *n_partials = blocks;
+  }
   return (int)hipGetLastError();
 }
 
