@@ -312,6 +312,8 @@ def summarize_rocprof(label: str, bench_args: str, pmc_args: str, out: str = "gp
         f.write(f"- step {j['ms_per_step'] * 1e3:.1f} us, {j['value'] / 1e9:.2f} G params/s\n")
         f.write("\nOnly this library's kernels and the calibration copy (`calib_copy`, a one-shot "
                 "copy of known size) are listed; torch's set-up kernels are left out.  "
+                "The reduce's deferred form (above N = 8, on up to 2^27 elements) is listed "
+                "under the one-chunk kernel's name (`k1_reduce_check`, `k1u_reduce_check`).  "
                 "Algorithmic bytes: 2N + 4 per element for the reduce, 30 for the update, "
                 "2N + 26 for the single pass.\n")
     with open(os.path.join(prof, f"{prefix}_{label}_hbm_traffic.md"), "w") as f:
