@@ -93,11 +93,13 @@ def test_random_configuration_matches_oracle(seed):
 
 def random_unit_workload(seed: int) -> synth.Workload:
     """A unit layout (ZeRO-3 / FSDP): 1-8 tensors in 1-8 contiguous units,
-    each unit flattened and sharded on its own; fp16 only."""
+    each unit flattened and sharded on its own; fp16 only.  Above N = 8 the
+    reduce's workgroups take eight chunks that may span several units."""
     rng = np.random.default_rng([0x7A3F, seed])
-    n = int(_pick(rng, [1, 2, 3, 4, 8, 16]))
+    n = int(_pick(rng, [1, 2, 3, 4, 8, 13, 16, 32]))
     n_t = int(rng.integers(1, 9))
-    tensors = tuple((f"t{i}", (int(rng.integers(1, 20_000)),)) for i in range(n_t))
+    tensors = tuple((f"t{i}", (int(rng.integers(1, 20_000 if rng.random() < 0.7 else 150_000)),))
+                    for i in range(n_t))
     n_u = int(rng.integers(1, n_t + 1))
     cuts = set(int(c) for c in rng.choice(np.arange(1, n_t), n_u - 1, replace=False)) \
         if n_u > 1 else set()
