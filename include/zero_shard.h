@@ -505,7 +505,7 @@ typedef struct zero_unit_buffers {
   float* v;                /* [shard] fp32, 16-byte aligned, in place */
   uint16_t* param16;       /* [shard] fp16 slot of this rank's piece, 2-byte aligned */
   int64_t shard;           /* S_u, elements (padding included) */
-  int64_t reduce_block;    /* first reduce workgroup: set by zero_units_prepare */
+  int64_t reduce_block;    /* first 512-element reduce chunk: set by zero_units_prepare */
   int64_t adam_block;      /* first Adam workgroup: set by zero_units_prepare */
 } zero_unit_buffers_t;
 
@@ -521,8 +521,9 @@ typedef struct zero_unit_buffers {
 int zero_units_prepare(zero_unit_buffers_t* units, int32_t n_units, int64_t* reduce_blocks_out,
                        int64_t* adam_blocks_out);
 
-/* Workspace bytes for a prepared table: 256 + 16 * (256 + reduce workgroups).
- * It needs no initialisation.  0 on bad input. */
+/* Workspace bytes for a prepared table: 256 + 16 * (256 + reduce chunks), the
+ * chunk total zero_units_prepare returns (above N = 8 the reduce may write
+ * fewer partials).  It needs no initialisation.  0 on bad input. */
 size_t zero_units_workspace_bytes(const zero_unit_buffers_t* units, int32_t n_units);
 
 /*
