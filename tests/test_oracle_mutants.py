@@ -41,6 +41,16 @@ MUTANTS = [
      "lo, hi = max(a, off), min(b, off + n)", "lo, hi = max(a, off), min(b, off + n + 1)"),
     ("unit rank offsets by unit length, not by shard", PY,
      "        roff += s\n", "        roff += p\n"),
+    ("unit shard not rounded up to the alignment", PY,
+     "s = -(-(-(-p // world_size)) // align) * align", "s = -(-p // world_size)"),
+    ("plan shard not rounded up to the alignment", PY,
+     "shard = -(-per_rank // align) * align", "shard = per_rank"),
+    ("unit element map one rank off", PY,
+     "local = np.arange(s, dtype=np.int64) + rank * s", "local = np.arange(s, dtype=np.int64) + (rank + 1) * s"),
+    ("unit lookup takes the unit before a boundary", PY,
+     'u = np.searchsorted(offs, pos, side="right") - 1', 'u = np.searchsorted(offs, pos, side="left") - 1'),
+    ("padding of a rank's shard counted as real", PY,
+     "return max(0, min(self.shard, self.psi - rank * self.shard))", "return self.shard"),
     # host scalars
     ("1 - beta1 rounded as 1f - 0.9f", PY,
      "omb1=F32(1.0 - beta1)", "omb1=F32(F32(1.0) - F32(beta1))"),
