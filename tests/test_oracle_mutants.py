@@ -190,10 +190,10 @@ def test_mutant_texts_apply_to_the_current_oracle():
 
 @pytest.mark.timeout(1200)
 def test_every_planted_mistake_fails_the_pins(tmp_path):
-    base = tmp_path / "clean"
-    _copy_tree(str(base))
-    rc, out = _run_pins(str(base), NUMPY_PINS + C_PINS)
-    assert rc == 0, "the unmodified copy fails its pins:\n" + out
+    def clean():
+        d = str(tmp_path / "clean")
+        _copy_tree(d)
+        return _run_pins(d, NUMPY_PINS + C_PINS)
 
     def one(i):
         name, path, old, new = MUTANTS[i]
@@ -206,7 +206,10 @@ def test_every_planted_mistake_fails_the_pins(tmp_path):
 
     workers = max(1, min(8, os.cpu_count() or 1))
     with ThreadPoolExecutor(workers) as ex:
+        base = ex.submit(clean)
         results = list(ex.map(one, range(len(MUTANTS))))
+        rc, out = base.result()
+    assert rc == 0, "the unmodified copy fails its pins:\n" + out
     missed = [(name, out) for name, rc, out in results if rc == 0]
     assert not missed, "mutants the pins did not catch:\n" + "\n".join(
         f"- {name}\n{out}" for name, out in missed)
