@@ -147,14 +147,14 @@ def test_units_one_pass_rejects_clipping_and_overlap():
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("w,rank,one_pass", [
     pytest.param(synth.LLAMA3_8B_FSDP, 0, False, id="llama3_8b_fsdp-r0"),
-    pytest.param(synth.GPT2_FSDP, 1, False, id="gpt2_1p5b_fsdp-r1"),
     pytest.param(dataclasses.replace(synth.LLAMA3_8B_FSDP, max_grad_norm=0.0), 0, True,
                  id="llama3_8b_fsdp-noclip-r0-1pass"),
     pytest.param(synth.GPT2_FSDP, 1, True, id="gpt2_1p5b_fsdp-r1-1pass")])
 def test_units_full_rank(w, rank, one_pass):
     """A whole rank of a many-unit layout (34 units for Llama-3-8B, 50 for
     GPT-2), every step: whole-rank Q, norm, coef and skip from the C oracle on
-    the same host chunks, and ~4k sampled elements bit for bit."""
+    the same host chunks, and ~4k sampled elements bit for bit (the two-pass
+    GPT-2 rank is compared at every element below)."""
     import zero_sharded_optimizer_rank_amd.abi as abi
     from zero_sharded_optimizer_rank_amd.units import DeviceUnits
 
@@ -203,6 +203,98 @@ def test_units_full_rank(w, rank, one_pass):
         assert all(x == 0 for x in rep.mismatches.values()), (step, rep.mismatches)
         assert dev.guards_intact()
         print(f"  step {step}: coef={float(fin.coef):.6g} norm={fin.norm:.6g}", flush=True)
+        abi.zero_scaler_update(scaler, bool(res.skip))
+        o_scale, o_good = oracle.scaler_update(o_scale, o_good, fin.skip)
+        o_t += 0 if fin.skip else 1
+    del dev
+    torch.cuda.empty_cache()
+
+
+def _units_host_state(dev):
+    """Per unit: the oracle's master (seeded real elements, +0 padding), m, v
+    and the fp16 slot, as the device starts."""
+    w, st = dev.w, []
+    for u, b in enumerate(dev.bufs):
+        s, real = b["shard"], dev.unit_real(u)
+        p = np.zeros(s, dtype=np.float32)
+        if real:
+            p[:real] = synth.masters(w, dev.unit_model_start(u), real)
+        st.append([p, np.zeros(s, np.float32), np.zeros(s, np.float32),
+                   fast.cast16(p)])
+    return st
+
+
+def _feed_units_every_element(dev, step, scale, inv32):
+    """Each unit's contributions, generated chunk by chunk, copied to its rows
+    and reduced by the C oracle: returns (Q, overflow, g of every element of
+    every unit, +0 in padding columns as on the device)."""
+    w, n = dev.w, dev.w.world_size
+    chunk = (1 << 27) // n
+    host = torch.empty((n, chunk), dtype=torch.int16, pin_memory=True)
+    hnp = host.numpy().view(np.uint16)
+    q_total, bad, gs = 0, False, []
+    for u, b in enumerate(dev.bufs):
+        real, start = dev.unit_real(u), dev.unit_model_start(u)
+        g = np.zeros(b["shard"], dtype=np.float32)
+        for c0 in range(0, real, chunk):
+            k = min(chunk, real - c0)
+            for q in range(n):
+                synth.contributions(w, step, q, start + c0, k, scale, out=hnp[q, :k])
+            with torch.cuda.stream(dev.stream):
+                for q in range(n):
+                    b["contrib"][q, c0:c0 + k].copy_(host[q, :k], non_blocking=True)
+            qc, bc = fast.reduce_stats(hnp, k)
+            q_total += qc
+            bad |= bc
+            fast.reduce_unscale(hnp, inv32, count=k, out=g[c0:c0 + k])
+            dev.stream.synchronize()
+        gs.append(g)
+    return q_total, bad, gs
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("rank", [1, 63])
+def test_units_full_rank_every_element(rank):
+    """A whole rank of GPT-2 in 50 units at N = 64 (the deferred unit reduce),
+    every step, every element of every unit: g, master, m, v and the slot bit
+    for bit against the C form of the oracle's unscale and update (pinned to
+    the numpy definitions); ranks 1 and 63 (the last).  Every GPT-2 unit
+    divides by 64, so these shards hold no padding; the padded unit layouts
+    are the tiny and sixteen-rank tests above."""
+    import zero_sharded_optimizer_rank_amd.abi as abi
+    from zero_sharded_optimizer_rank_amd.units import DeviceUnits
+
+    w = synth.GPT2_FSDP
+    print(f"[units every element {w.name} rank {rank}]", flush=True)
+    dev = DeviceUnits(w, rank)
+    dev.load_initial_state()
+    st = _units_host_state(dev)
+    scaler = abi.new_scaler(w.loss_scale0)
+    o_scale, o_good, o_t = w.loss_scale0, 0, 0
+    for step in range(1, w.steps + 1):
+        sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, o_t + 1, w.world_size,
+                                 o_scale)
+        q_all, bad_all, gs = _feed_units_every_element(dev, step, scaler.scale, sc.inv32)
+        dev.step(dev.args(scaler.t + 1, scaler.scale))
+        res = dev.result()
+        fin = oracle.finalize(q_all, bad_all, sc.inv64, w.max_grad_norm)
+        check_result(res, fin, step)
+        if not fin.skip:
+            for u in range(dev.n_units):
+                fast.adam_update(gs[u], *st[u], sc, fin.coef)
+        for u, b in enumerate(dev.bufs):
+            s = b["shard"]
+            got = {"grad": b["grad"][:s], "master": b["master"][:s], "m": b["m"][:s],
+                   "v": b["v"][:s]}
+            want = {"grad": gs[u], "master": st[u][0], "m": st[u][1], "v": st[u][2]}
+            for name in got:
+                d = got[name].cpu().numpy()
+                assert fast.count_unequal(d, want[name]) == 0, (step, u, name)
+            slot = dev.slot(u).cpu().numpy().view(np.uint16)
+            assert fast.count_unequal(slot, st[u][3]) == 0, (step, u, "slot")
+        assert dev.guards_intact()
+        print(f"  step {step}: coef={float(fin.coef):.6g} norm={fin.norm:.6g}, "
+              f"{sum(b['shard'] for b in dev.bufs)} elements equal", flush=True)
         abi.zero_scaler_update(scaler, bool(res.skip))
         o_scale, o_good = oracle.scaler_update(o_scale, o_good, fin.skip)
         o_t += 0 if fin.skip else 1
