@@ -146,7 +146,6 @@ def test_units_one_pass_rejects_clipping_and_overlap():
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("w,rank,one_pass", [
-    pytest.param(synth.LLAMA3_8B_FSDP, 0, False, id="llama3_8b_fsdp-r0"),
     pytest.param(dataclasses.replace(synth.LLAMA3_8B_FSDP, max_grad_norm=0.0), 0, True,
                  id="llama3_8b_fsdp-noclip-r0-1pass"),
     pytest.param(synth.GPT2_FSDP, 1, True, id="gpt2_1p5b_fsdp-r1-1pass")])
@@ -154,7 +153,7 @@ def test_units_full_rank(w, rank, one_pass):
     """A whole rank of a many-unit layout (34 units for Llama-3-8B, 50 for
     GPT-2), every step: whole-rank Q, norm, coef and skip from the C oracle on
     the same host chunks, and ~4k sampled elements bit for bit (the two-pass
-    GPT-2 rank is compared at every element below)."""
+    ranks are compared at every element below)."""
     import zero_sharded_optimizer_rank_amd.abi as abi
     from zero_sharded_optimizer_rank_amd.units import DeviceUnits
 
@@ -253,31 +252,36 @@ def _feed_units_every_element(dev, step, scale, inv32):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("rank", [1, 63])
-def test_units_full_rank_every_element(rank):
-    """A whole rank of GPT-2 in 50 units at N = 64 (the deferred unit reduce),
-    every step, every element of every unit: g, master, m, v and the slot bit
-    for bit against the C form of the oracle's unscale and update (pinned to
-    the numpy definitions); ranks 1 and 63 (the last).  Every GPT-2 unit
-    divides by 64, so these shards hold no padding; the padded unit layouts
+@pytest.mark.parametrize("w,rank", [
+    pytest.param(synth.GPT2_FSDP, 1, id="gpt2_1p5b_fsdp-r1"),
+    pytest.param(synth.GPT2_FSDP, 63, id="gpt2_1p5b_fsdp-r63"),
+    pytest.param(synth.LLAMA3_8B_FSDP, 0, id="llama3_8b_fsdp-r0")])
+def test_units_full_rank_every_element(w, rank):
+    """A whole rank of a many-unit layout, every step, every element of every
+    unit: g, master, m, v and the slot bit for bit against the C form of the
+    oracle's unscale and update (pinned to the numpy definitions).  GPT-2 in
+    50 units at N = 64 runs the deferred unit reduce (ranks 1 and 63, the
+    last); Llama-3-8B in 34 units at N = 8 the one-chunk reduce, with
+    clipping and the other ranks' share of the norm.  Every unit of both
+    divides by N, so these shards hold no padding; the padded unit layouts
     are the tiny and sixteen-rank tests above."""
     import zero_sharded_optimizer_rank_amd.abi as abi
     from zero_sharded_optimizer_rank_amd.units import DeviceUnits
 
-    w = synth.GPT2_FSDP
     print(f"[units every element {w.name} rank {rank}]", flush=True)
     dev = DeviceUnits(w, rank)
     dev.load_initial_state()
     st = _units_host_state(dev)
+    other_sq = w.other_sq(dev.real_count()) if w.other_ranks_from_config else 0.0
     scaler = abi.new_scaler(w.loss_scale0)
     o_scale, o_good, o_t = w.loss_scale0, 0, 0
     for step in range(1, w.steps + 1):
         sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, o_t + 1, w.world_size,
                                  o_scale)
         q_all, bad_all, gs = _feed_units_every_element(dev, step, scaler.scale, sc.inv32)
-        dev.step(dev.args(scaler.t + 1, scaler.scale))
+        dev.step(dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq))
         res = dev.result()
-        fin = oracle.finalize(q_all, bad_all, sc.inv64, w.max_grad_norm)
+        fin = oracle.finalize(q_all, bad_all, sc.inv64, w.max_grad_norm, other_sq=other_sq)
         check_result(res, fin, step)
         if not fin.skip:
             for u in range(dev.n_units):
