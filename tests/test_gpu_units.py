@@ -9,9 +9,8 @@ import pytest
 import oracle
 import synth
 from oracle import fast
-from oracle import run as orun
 
-from parity_util import check_result, compare_state, run_units_all_ranks, StepReport
+from parity_util import check_result, run_units_all_ranks
 
 pytestmark = pytest.mark.gpu
 
@@ -68,35 +67,6 @@ def test_units_deferred_reduce_all_ranks(variant):
         assert [r.skip for r in reports] == [s == 2 for s in range(1, w.steps + 1)]
 
 
-def _feed_units_and_reduce(dev, step, scale, pos):
-    """Generate each unit's contributions chunk by chunk, copy them to the
-    unit's rows and reduce the same host chunks with the C oracle.  Returns
-    (Q, overflow, contributions at the sampled positions)."""
-    w, n = dev.w, dev.w.world_size
-    chunk = (1 << 27) // n
-    host = torch.empty((n, chunk), dtype=torch.int16, pin_memory=True)
-    hnp = host.numpy().view(np.uint16)
-    q_total, bad = 0, False
-    cols = np.zeros((n, pos.size), dtype=np.uint16)
-    pu, pj = dev.locate(pos)
-    for u, b in enumerate(dev.bufs):
-        real, start = dev.unit_real(u), dev.unit_model_start(u)
-        for c0 in range(0, real, chunk):
-            k = min(chunk, real - c0)
-            for q in range(n):
-                synth.contributions(w, step, q, start + c0, k, scale, out=hnp[q, :k])
-            with torch.cuda.stream(dev.stream):
-                for q in range(n):
-                    b["contrib"][q, c0:c0 + k].copy_(host[q, :k], non_blocking=True)
-            qc, bc = fast.reduce_stats(hnp, k)
-            q_total += qc
-            bad |= bc
-            sel = (pu == u) & (pj >= c0) & (pj < c0 + k)
-            cols[:, sel] = hnp[:, pj[sel] - c0]
-            dev.stream.synchronize()
-    return q_total, bad, cols
-
-
 @pytest.mark.parametrize("variant", ["config", "skip"])
 def test_tiny_fsdp_all_ranks_one_pass(variant):
     """The unit single pass on all four tiny ranks: every rank's pass, then
@@ -144,71 +114,6 @@ def test_units_one_pass_rejects_clipping_and_overlap():
     assert e.value.code == abi.ZERO_EINVAL
 
 
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("w,rank,one_pass", [
-    pytest.param(dataclasses.replace(synth.LLAMA3_8B_FSDP, max_grad_norm=0.0), 0, True,
-                 id="llama3_8b_fsdp-noclip-r0-1pass"),
-    pytest.param(synth.GPT2_FSDP, 1, True, id="gpt2_1p5b_fsdp-r1-1pass")])
-def test_units_full_rank(w, rank, one_pass):
-    """A whole rank of a many-unit layout (34 units for Llama-3-8B, 50 for
-    GPT-2), every step: whole-rank Q, norm, coef and skip from the C oracle on
-    the same host chunks, and ~4k sampled elements bit for bit (the two-pass
-    ranks are compared at every element below)."""
-    import zero_sharded_optimizer_rank_amd.abi as abi
-    from zero_sharded_optimizer_rank_amd.units import DeviceUnits
-
-    print(f"[units full rank {w.name} rank {rank} one_pass={one_pass}]", flush=True)
-    dev = DeviceUnits(w, rank, one_pass=one_pass)
-    dev.load_initial_state()
-    up = orun.workload_unit_plan(w)
-    assert dev.plan.rank_shard == up.rank_shard
-    rng = np.random.default_rng(rank + 100)
-    offs = np.array(up.unit_rank_offset)
-    pos = np.unique(np.concatenate([rng.integers(0, up.rank_shard, 4096), offs,
-                                    np.minimum(offs + 3, up.rank_shard - 1),
-                                    np.arange(up.rank_shard - 16, up.rank_shard)]))
-    e = oracle.unit_model_index(up, rank, pos)
-    op = np.array([synth.masters(w, int(x), 1)[0] if x >= 0 else 0.0 for x in e],
-                  dtype=np.float32)
-    om, ov = np.zeros_like(op), np.zeros_like(op)
-    oh = op.astype(np.float16).view(np.uint16)
-    real = dev.real_count()
-    other_sq = w.other_sq(real) if w.other_ranks_from_config else 0.0
-    scaler = abi.new_scaler(w.loss_scale0)
-    o_scale, o_good, o_t = w.loss_scale0, 0, 0
-    for step in range(1, w.steps + 1):
-        q_all, bad_all, cols = _feed_units_and_reduce(dev, step, scaler.scale, pos)
-        if one_pass:
-            dev.step_1pass(dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq))
-        else:
-            dev.step(dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq))
-        res = dev.result()
-        if one_pass and not res.skip:
-            dev.adopt()
-        sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, o_t + 1, w.world_size,
-                                 o_scale)
-        fin = oracle.finalize(q_all, bad_all, sc.inv64, w.max_grad_norm, other_sq=other_sq)
-        check_result(res, fin, step)
-        acc = oracle.reduce_contributions(cols)
-        g = oracle.unscale(acc, sc.inv32)
-        if not one_pass:
-            assert np.array_equal(_bits(dev.fetch_at("grad", pos)), _bits(g)), step
-        if not fin.skip:
-            op, om, ov, h = oracle.adam_apply(g, op, om, ov, sc, fin.coef)
-            oh = h.view(np.uint16)
-        rep = StepReport(step, fin.skip, float(fin.coef))
-        for name, want in (("master", op), ("m", om), ("v", ov), ("slot", oh)):
-            compare_state(rep, name, dev.fetch_at(name, pos), want)
-        assert all(x == 0 for x in rep.mismatches.values()), (step, rep.mismatches)
-        assert dev.guards_intact()
-        print(f"  step {step}: coef={float(fin.coef):.6g} norm={fin.norm:.6g}", flush=True)
-        abi.zero_scaler_update(scaler, bool(res.skip))
-        o_scale, o_good = oracle.scaler_update(o_scale, o_good, fin.skip)
-        o_t += 0 if fin.skip else 1
-    del dev
-    torch.cuda.empty_cache()
-
-
 def _units_host_state(dev):
     """Per unit: the oracle's master (seeded real elements, +0 padding), m, v
     and the fp16 slot, as the device starts."""
@@ -252,24 +157,30 @@ def _feed_units_every_element(dev, step, scale, inv32):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("w,rank", [
-    pytest.param(synth.GPT2_FSDP, 1, id="gpt2_1p5b_fsdp-r1"),
-    pytest.param(synth.GPT2_FSDP, 63, id="gpt2_1p5b_fsdp-r63"),
-    pytest.param(synth.LLAMA3_8B_FSDP, 0, id="llama3_8b_fsdp-r0")])
-def test_units_full_rank_every_element(w, rank):
+@pytest.mark.parametrize("w,rank,one_pass", [
+    pytest.param(synth.GPT2_FSDP, 1, False, id="gpt2_1p5b_fsdp-r1"),
+    pytest.param(synth.GPT2_FSDP, 63, False, id="gpt2_1p5b_fsdp-r63"),
+    pytest.param(synth.LLAMA3_8B_FSDP, 0, False, id="llama3_8b_fsdp-r0"),
+    pytest.param(synth.GPT2_FSDP, 1, True, id="gpt2_1p5b_fsdp-r1-1pass"),
+    pytest.param(dataclasses.replace(synth.LLAMA3_8B_FSDP, max_grad_norm=0.0), 0, True,
+                 id="llama3_8b_fsdp-noclip-r0-1pass")])
+def test_units_full_rank_every_element(w, rank, one_pass):
     """A whole rank of a many-unit layout, every step, every element of every
-    unit: g, master, m, v and the slot bit for bit against the C form of the
-    oracle's unscale and update (pinned to the numpy definitions).  GPT-2 in
-    50 units at N = 64 runs the deferred unit reduce (ranks 1 and 63, the
-    last); Llama-3-8B in 34 units at N = 8 the one-chunk reduce, with
-    clipping and the other ranks' share of the norm.  Every unit of both
-    divides by N, so these shards hold no padding; the padded unit layouts
-    are the tiny and sixteen-rank tests above."""
+    unit: g (two-pass step), master, m, v and the slot bit for bit against
+    the C form of the oracle's unscale and update (pinned to the numpy
+    definitions), and the whole-rank Q, norm, coef and skip from the C
+    oracle's reduce statistics on the same host chunks.  GPT-2 in 50 units at
+    N = 64 runs the deferred unit reduce (ranks 1 and 63, the last);
+    Llama-3-8B in 34 units at N = 8 the one-chunk reduce, with clipping and
+    the other ranks' share of the norm; the single pass over all units on
+    both, its new set adopted after each step.  Every unit of both divides by
+    N, so these shards hold no padding; the padded unit layouts are the tiny
+    and sixteen-rank tests above."""
     import zero_sharded_optimizer_rank_amd.abi as abi
     from zero_sharded_optimizer_rank_amd.units import DeviceUnits
 
-    print(f"[units every element {w.name} rank {rank}]", flush=True)
-    dev = DeviceUnits(w, rank)
+    print(f"[units every element {w.name} rank {rank} one_pass={one_pass}]", flush=True)
+    dev = DeviceUnits(w, rank, one_pass=one_pass)
     dev.load_initial_state()
     st = _units_host_state(dev)
     other_sq = w.other_sq(dev.real_count()) if w.other_ranks_from_config else 0.0
@@ -279,8 +190,14 @@ def test_units_full_rank_every_element(w, rank):
         sc = oracle.step_scalars(w.lr, *w.betas, w.eps, w.weight_decay, o_t + 1, w.world_size,
                                  o_scale)
         q_all, bad_all, gs = _feed_units_every_element(dev, step, scaler.scale, sc.inv32)
-        dev.step(dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq))
+        args = dev.args(scaler.t + 1, scaler.scale, other_sq=other_sq)
+        if one_pass:
+            dev.step_1pass(args)
+        else:
+            dev.step(args)
         res = dev.result()
+        if one_pass and not res.skip:
+            dev.adopt()
         fin = oracle.finalize(q_all, bad_all, sc.inv64, w.max_grad_norm, other_sq=other_sq)
         check_result(res, fin, step)
         if not fin.skip:
@@ -292,6 +209,8 @@ def test_units_full_rank_every_element(w, rank):
                    "v": b["v"][:s]}
             want = {"grad": gs[u], "master": st[u][0], "m": st[u][1], "v": st[u][2]}
             for name in got:
+                if one_pass and name == "grad":
+                    continue  # the single pass writes no g
                 d = got[name].cpu().numpy()
                 assert fast.count_unequal(d, want[name]) == 0, (step, u, name)
             slot = dev.slot(u).cpu().numpy().view(np.uint16)
