@@ -538,7 +538,9 @@ size_t zero_units_workspace_bytes(const zero_unit_buffers_t* units, int32_t n_un
  *               `stream` (passed by value through a small kernel's
  *               arguments) ahead of the kernels that read it, so the kernels
  *               only ever see the table checked on the host; its content on
- *               entry does not matter
+ *               entry does not matter.  Calls in flight at the same time on
+ *               different streams need their own units_dev (as they need
+ *               their own workspace): each call rewrites it.
  *   workspace, dev_result, args, stream: as in the flat calls
  * Errors: as the flat calls, plus ZERO_EINVAL when units_host was not
  * prepared or units_dev is NULL, ZERO_EALIGN for a misaligned units_dev.
