@@ -85,7 +85,8 @@ def other_overflow_at(w: synth.Workload, step: int, flat_begin: int, count: int)
 def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Optional[int] = None,
                fused: bool = True, strict: bool = True,
                ws_fill: Optional[int] = None, offload: Optional[dict] = None,
-               one_pass: bool = False, in_place_slot: bool = False) -> List[StepReport]:
+               one_pass: bool = False, in_place_slot: bool = False,
+               stream=None) -> List[StepReport]:
     """Run `steps` steps of the workload on one window of rank's shard on the
     GPU and in the oracle; compare every step.  With `offload` (OffloadShard
     keyword arguments) the update runs in the offload form: host state, PCIe
@@ -93,7 +94,8 @@ def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Opti
     zero_reduce_adam_step_1pass into the second state set, adopted only when
     the step was not skipped; no gradient is written, so none is compared.
     With `in_place_slot` as well, the pass writes the live slot and
-    zero_slot_restore follows every step."""
+    zero_slot_restore follows every step.  `stream`: the torch stream every
+    call of the window runs on (default: the thread's current stream)."""
     import zero_sharded_optimizer_rank_amd.abi as abi
     from zero_sharded_optimizer_rank_amd.shard import DeviceShard, OffloadShard
 
@@ -101,7 +103,7 @@ def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Opti
     if offload is not None:
         dev = OffloadShard(w, rank, begin, count, **offload)
     else:
-        dev = DeviceShard(w, rank, begin, count, one_pass=one_pass)
+        dev = DeviceShard(w, rank, begin, count, one_pass=one_pass, stream=stream)
     dev.load_initial_state()
     p = orun.workload_plan(w)
     flat_begin = rank * p.shard + begin
@@ -163,7 +165,8 @@ def run_window(w: synth.Workload, rank: int, begin: int, count: int, steps: Opti
 
 
 def run_units_all_ranks(w: synth.Workload, max_norm: Optional[float] = None,
-                        one_pass: bool = False, in_place_slot: bool = False) -> List[StepReport]:
+                        one_pass: bool = False, in_place_slot: bool = False,
+                        stream=None) -> List[StepReport]:
     """Every rank of a unit layout on the GPU (zero_units_* through DeviceUnits)
     and in the oracle, all steps, with the exact all-reduce of the squared-norm
     integers and overflow flags between the ranks; every rank's g, result and
@@ -178,7 +181,7 @@ def run_units_all_ranks(w: synth.Workload, max_norm: Optional[float] = None,
     max_norm = w.max_grad_norm if max_norm is None else max_norm
     n = w.world_size
     up = orun.workload_unit_plan(w)
-    devs = [DeviceUnits(w, r, one_pass=one_pass, in_place_slot=in_place_slot)
+    devs = [DeviceUnits(w, r, one_pass=one_pass, in_place_slot=in_place_slot, stream=stream)
             for r in range(n)]
     for d in devs:
         d.load_initial_state()
