@@ -324,3 +324,41 @@ def test_units_step_other_overflow_launches_no_update():
         assert np.array_equal(_bits(a.fetch(name)), _bits(want)), name
         assert np.array_equal(_bits(b.fetch(name)), _bits(want)), name
     assert np.array_equal(_bits(a.fetch("grad")), _bits(b.fetch("grad")))
+
+
+@pytest.mark.parametrize("n", [4, 16])
+def test_units_with_empty_units_all_ranks(n):
+    """Units holding no elements (a tensor of size 0 as its own unit) between
+    real ones, at N = 4 (one-chunk reduce) and N = 16 (deferred reduce): each
+    empty unit still takes one reduce chunk that must write and count
+    nothing; every rank bit for bit, with a skipped step."""
+    print(f"[units with empty units N={n}]", flush=True)
+    w = dataclasses.replace(
+        synth.TINY_FSDP, name=f"units_empty_{n}", cfg_id=60 + n, world_size=n,
+        tensors=(("z0", (0,)), ("a", (3000,)), ("z1", (0,)), ("b", (70_000,)), ("z2", (0,)),
+                 ("c", (5,)), ("z3", (0,))),
+        units=(0, 1, 2, 3, 4, 5, 6), parity_ranks=tuple(range(n)), inject_step=2)
+    reports = run_units_all_ranks(w, 1.0)
+    assert [r.skip for r in reports] == [s == 2 for s in range(1, w.steps + 1)]
+
+
+def test_units_no_units():
+    """n_units = 0: the step checks its arguments, launches only the finalize
+    (Q = 0, nothing overflowed) and writes the result word."""
+    import zero_sharded_optimizer_rank_amd.abi as abi
+
+    print("[units: no units]", flush=True)
+    dev = torch.device("cuda:0")
+    table = abi.unit_table(0)
+    table_dev = torch.empty(8, dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(abi.zero_units_workspace_bytes(table, 0), 16), dtype=torch.uint8,
+                     device=dev)
+    res = torch.full((abi.RESULT_BYTES,), 0xAB, dtype=torch.uint8, device=dev)
+    args = abi.step_args(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                         max_grad_norm=1.0, loss_scale=1024.0, step=1, other_sq=0.25)
+    abi.zero_units_step(4, table, table_dev, 0, args, ws, ws.numel(), res)
+    torch.cuda.synchronize()
+    r = abi.zero_step_result_t.from_buffer_copy(res.cpu().numpy().tobytes())
+    fin = oracle.finalize(0, False, 1.0 / (4 * 1024.0), 1.0, other_sq=0.25)
+    check_result(r, fin, 1)
+    assert not r.skip
