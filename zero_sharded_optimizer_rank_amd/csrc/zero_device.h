@@ -82,34 +82,46 @@
 #ifndef ZK_K1_LDS
 #define ZK_K1_LDS 16384
 #endif
-// Above N = 8, on shards of up to ZK_K1_DEFER_MAX_SHARD elements, the reduce
-// defers its gradient stores: each workgroup sums ZK_K1_DEFER consecutive
-// 512-element chunks one after the other, holding the chunks' g quads in
-// registers, and stores them all at the end.  With 64 rows the rows are 97%
-// of the bytes, and the small g stream spread evenly among them slows the
-// reads far more than its own size: on the flat 7.5B shard's geometry,
-// reading the 64 rows alone took 2.12 ms, with the g stores after every
-// chunk 2.46-2.48 ms, with 8 or 16 chunks' stores deferred 2.35 and 2.30 ms
-// (no-arithmetic probes, 8 workgroups per CU); 8 chunks per workgroup without
-// the deferral ran at 2.71 ms.  The built kernel (8 chunks, 9 workgroups per
-// CU) against the one-chunk form at N = 64, interleaved on the same buffers:
-// S = 24 M (GPT-2) 0.480 / 0.524 ms, 60 M 1.228 / 1.269, 117 M (flat 7.5B)
-// 2.415 / 2.466; but S = 250 M 5.63 / 5.38, 500 M 11.46 / 10.66 and 1.08 G
-// (Llama-2-70B) 24.4 / 23.3 ms, so larger shards keep one chunk per
-// workgroup.  At N = 16 and 32 the deferral did not help in the probes, so
-// N <= 8 keeps one chunk per workgroup too.  The unit reduce defers under
-// the same rule on the units' total: GPT-2 in 50 units at N = 64, 0.514
-// against 0.527 ms (8 chunks at 8 / 10 / 12 per CU 0.554 / 0.525 / 0.554,
-// 16 chunks at 8 / 9 per CU 0.566 / 0.581, 4 chunks at 10 / 12 per CU 0.535
-// / 0.542).
+// Above N = 8 the reduce defers its gradient stores: each workgroup sums
+// ZK_K1_DEFER consecutive 512-element chunks one after the other, holding
+// the chunks' g quads in registers, and stores them all at the end.  With 64
+// rows the rows are 97% of the bytes, and the small g stream spread evenly
+// among them slows the reads far more than its own size: on the flat 7.5B
+// shard's geometry, reading the 64 rows alone took 2.12 ms, with the g
+// stores after every chunk 2.46-2.48 ms, with 8 or 16 chunks' stores
+// deferred 2.35 and 2.30 ms (no-arithmetic probes, 8 workgroups per CU); 8
+// chunks per workgroup without the deferral ran at 2.71 ms.  In one launch
+// over the whole shard the deferral only paid up to about 2^27 elements (S =
+// 24 M 0.480 against 0.524 ms, 117 M 2.415 / 2.466, but 250 M 5.63 / 5.38,
+// 1.08 G 24.4 / 23.3); issued in launches of ZK_K1_DEFER_SEG_ELEMS elements
+// (see launch_segments) it pays at every length.  At N = 8 it did not pay
+// (3.17-3.42 against 3.08-3.10 ms on Llama-3-8B, deferring 2, 4 or 8 chunks).
 #ifndef ZK_K1_DEFER
 #define ZK_K1_DEFER 8
 #endif
 #ifndef ZK_K1_DEFER_LDS
 #define ZK_K1_DEFER_LDS 18176
 #endif
-#ifndef ZK_K1_DEFER_MAX_SHARD
-#define ZK_K1_DEFER_MAX_SHARD ((int64_t)1 << 27)
+// Elements per launch of the streaming kernels.  A one-shot grid streams
+// more slowly the longer it runs; the same workgroups issued as several
+// launches back to back on the stream (launch_segments) run faster.  Each
+// form was measured through windows of one shard (interleaved, same
+// buffers): the deferred reduce at N = 64 in launches of 2^25 elements
+// against one launch: Llama-2-70B 22.02 against 23.27 ms (one-chunk form),
+// S = 250 M 4.96 / 5.30, the flat 7.5B shard 2.26 / 2.41 (2^24: 2.25, 2^26:
+// 2.31); the one-chunk reduce at N = 8 in launches of 2^28: 3.08 against
+// 3.16 ms (2^27: 3.12, 2^26: 3.18; shorter ones lose to the launch gaps);
+// the update in launches of 2^26-2^28: 4.55 against 4.60 ms.  A plain copy
+// gains nothing from it (6.73 against 6.71 TB/s in two launches, less in
+// more).
+#ifndef ZK_K1_SEG_ELEMS
+#define ZK_K1_SEG_ELEMS ((int64_t)1 << 28)
+#endif
+#ifndef ZK_K1_DEFER_SEG_ELEMS
+#define ZK_K1_DEFER_SEG_ELEMS ((int64_t)1 << 25)
+#endif
+#ifndef ZK_K2_SEG_ELEMS
+#define ZK_K2_SEG_ELEMS ((int64_t)1 << 27)
 #endif
 // The single-pass kernel (reduce and update in one pass, steps without
 // clipping) streams N + 3 inputs and 4 outputs.  One-wave workgroups, 16 per
@@ -152,6 +164,20 @@ namespace dev {
 // Reserved LDS of a reduce launch over n contribution rows.
 inline unsigned k1_lds(int n) { return n <= 8 ? ZK_K1_LDS_SMALL_N : ZK_K1_LDS; }
 inline unsigned k12_lds(int n) { return n <= 8 ? ZK_K12_LDS_SMALL_N : ZK_K12_LDS; }
+
+// Issue a one-shot grid of `blocks` workgroups as launches of at most `seg`
+// workgroups each, in order on one stream: launch(b0, nb) launches
+// workgroups b0 .. b0 + nb - 1 (the kernels add b0 to blockIdx.x).
+template <typename Launch>
+inline int launch_segments(int64_t blocks, int64_t seg, Launch launch) {
+  if (seg < 1) seg = 1;
+  for (int64_t b0 = 0; b0 < blocks; b0 += seg) {
+    launch(b0, blocks - b0 < seg ? blocks - b0 : seg);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  return (int)hipSuccess;
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

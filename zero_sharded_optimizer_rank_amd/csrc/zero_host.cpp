@@ -620,10 +620,9 @@ int zero_units_reduce_check(int32_t world_size, const zero_unit_buffers_t* units
     return hip_status(zk::launch_finalize_empty(fa, dev_result, stream), "finalize launch");
   rc = upload_table(units_dev, units_host, n_units, stream);
   if (rc) return rc;
-  int64_t elems = 0, n_partials = 0;
-  for (int32_t u = 0; u < n_units; ++u) elems += units_host[u].shard;
-  rc = hip_status(zk::launch_units_reduce(units_dev, n_units, b1, elems, world_size,
-                                          (float)fa.inv64, workspace, &n_partials, stream),
+  int64_t n_partials = 0;
+  rc = hip_status(zk::launch_units_reduce(units_dev, n_units, b1, world_size, (float)fa.inv64,
+                                          workspace, &n_partials, stream),
                   "units reduce launch");
   if (rc) return rc;
   return hip_status(zk::launch_partials_finalize(workspace, n_partials, fa, dev_result, stream),

@@ -86,11 +86,11 @@ int launch_adam_bf16(const float* grad, float* master, float* m, float* v, uint1
 // launch_store_table writes a host table there through kernel arguments.
 int launch_store_table(const zero_unit_buffers_t* units_host, int32_t n_units,
                        zero_unit_buffers_t* units_dev, hipStream_t stream);
-// `blocks` is the one-chunk workgroup count zero_units_prepare recorded and
-// `elems` the units' total shard; *n_partials receives the partials written
-// (fewer when the deferred form runs).
+// `blocks` is the one-chunk workgroup count zero_units_prepare recorded;
+// *n_partials receives the partials written (fewer when the deferred form
+// runs, above N = 8).
 int launch_units_reduce(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
-                        int64_t elems, int n, float inv32, void* workspace, int64_t* n_partials,
+                        int n, float inv32, void* workspace, int64_t* n_partials,
                         hipStream_t stream);
 int launch_units_adam(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
                       const AdamScalars& sc, const zero_step_result_t* res, hipStream_t stream);

@@ -19,7 +19,9 @@
 // K1, K2 and K12 stream every element once and use one-shot grids: each thread
 // owns one 4-element quad (no grid-stride loop), so workgroups are dispatched
 // in address order and retire as they finish; on MI355X this streams
-// measurably faster than persistent grids.  Every load or store instruction
+// measurably faster than persistent grids.  Long grids of K1 and K2 go out as
+// several launches of consecutive workgroups (launch_segments), which streams
+// faster still.  Every load or store instruction
 // of a wave covers 512 bytes to 1 KiB contiguous, with nontemporal hints.
 // Nothing here is a dense contraction, so no matrix cores are used; HBM
 // bandwidth bounds K1, K2 and K12.  The per-quad bodies live in zero_device.h.
@@ -35,29 +37,33 @@ struct ContribTable {
   __device__ __forceinline__ const uint16_t* row(int r) const { return p[r]; }
 };
 
+// b0: the first workgroup of this launch (a long grid runs as several
+// launches; see launch_segments).
 __global__ __launch_bounds__(ZK_K1_THREADS) void k1_reduce_check(ContribTable ct, int32_t n,
                                                                  int64_t shard, float inv32,
                                                                  float* __restrict__ grad,
                                                                  Partial* __restrict__ partials,
-                                                                 uint32_t* __restrict__ ticket) {
+                                                                 uint32_t* __restrict__ ticket,
+                                                                 int64_t b0) {
+  const int64_t b = b0 + blockIdx.x;
   // KF runs after this kernel on the same stream: arm its ticket here, so the
   // workspace needs no initialisation by the caller.
-  if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
-  const int64_t q_first = (int64_t)blockIdx.x * ZK_K1_THREADS * ZK_K1_QUADS;
+  if (b == 0 && threadIdx.x == 0) *ticket = 0u;
+  const int64_t q_first = b * ZK_K1_THREADS * ZK_K1_QUADS;
   const Partial pt = reduce_block(ct, n, shard, q_first, inv32, grad);
-  if (threadIdx.x == 0) partials[blockIdx.x] = pt;
+  if (threadIdx.x == 0) partials[b] = pt;
 }
 
-// K1 above N = 8 on shards up to ZK_K1_DEFER_MAX_SHARD: each workgroup covers
-// ZK_K1_DEFER chunks and stores their gradients together at the end (see
-// reduce_block_deferred).
+// K1 above N = 8: each workgroup covers ZK_K1_DEFER chunks and stores their
+// gradients together at the end (see reduce_block_deferred).
 __global__ __launch_bounds__(ZK_K1_THREADS) void k1_reduce_check_deferred(
     ContribTable ct, int32_t n, int64_t shard, float inv32, float* __restrict__ grad,
-    Partial* __restrict__ partials, uint32_t* __restrict__ ticket) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
-  const int64_t q_first = (int64_t)blockIdx.x * ZK_K1_THREADS * ZK_K1_DEFER;
+    Partial* __restrict__ partials, uint32_t* __restrict__ ticket, int64_t b0) {
+  const int64_t b = b0 + blockIdx.x;
+  if (b == 0 && threadIdx.x == 0) *ticket = 0u;
+  const int64_t q_first = b * ZK_K1_THREADS * ZK_K1_DEFER;
   const Partial pt = reduce_block_deferred<ZK_K1_DEFER>(ct, n, shard, q_first, inv32, grad);
-  if (threadIdx.x == 0) partials[blockIdx.x] = pt;
+  if (threadIdx.x == 0) partials[b] = pt;
 }
 
 __global__ __launch_bounds__(kThreads) void kf_reduce_finalize(
@@ -71,16 +77,17 @@ __global__ void k_finalize(FinalizeArgs fa, zero_step_result_t* res) {
     finalize_into(res->own_q_lo, res->own_q_hi, (uint32_t)res->overflow, fa, res);
 }
 
-// Thread t of workgroup b owns quads (b*Q + u)*T + t, u < Q.
+// Thread t of workgroup b = b0 + blockIdx.x owns quads (b*Q + u)*T + t, u < Q.
 __global__ __launch_bounds__(ZK_K2_THREADS) void k2_adam(
     const float* __restrict__ grad, float* __restrict__ master, float* __restrict__ mom,
     float* __restrict__ var, uint16_t* __restrict__ slot, int64_t shard, AdamScalars sc,
-    const zero_step_result_t* __restrict__ res) {
+    const zero_step_result_t* __restrict__ res, int64_t b0) {
   if (res->skip) return;
   const float c = res->clip_coef;
+  const int64_t b = b0 + blockIdx.x;
 #pragma unroll
   for (int u = 0; u < ZK_K2_QUADS; ++u) {
-    const int64_t qd = ((int64_t)blockIdx.x * ZK_K2_QUADS + u) * ZK_K2_THREADS + threadIdx.x;
+    const int64_t qd = (b * ZK_K2_QUADS + u) * ZK_K2_THREADS + threadIdx.x;
     adam_quad(grad, master, mom, var, slot, shard, qd, c, sc);
   }
 }
@@ -152,12 +159,13 @@ __global__ void k_finalize_bf16(FinalizeArgs fa, zero_step_result_t* res) {
 __global__ __launch_bounds__(ZK_K2_THREADS) void k2_adam_bf16(
     const float* __restrict__ grad, float* __restrict__ master, float* __restrict__ mom,
     float* __restrict__ var, uint16_t* __restrict__ slot, int64_t shard, AdamScalars sc,
-    const zero_step_result_t* __restrict__ res) {
+    const zero_step_result_t* __restrict__ res, int64_t b0) {
   if (res->skip) return;
   const float c = res->clip_coef;
+  const int64_t b = b0 + blockIdx.x;
 #pragma unroll
   for (int u = 0; u < ZK_K2_QUADS; ++u) {
-    const int64_t qd = ((int64_t)blockIdx.x * ZK_K2_QUADS + u) * ZK_K2_THREADS + threadIdx.x;
+    const int64_t qd = (b * ZK_K2_QUADS + u) * ZK_K2_THREADS + threadIdx.x;
     adam_quad<Fmt::BF16>(grad, master, mom, var, slot, shard, qd, c, sc);
   }
 }
@@ -246,17 +254,25 @@ int launch_reduce_check(const uint16_t* const* contrib, int n, int64_t shard, fl
                         zero_step_result_t* res, hipStream_t stream) {
   ContribTable ct;
   for (int r = 0; r < ZERO_MAX_RANKS; ++r) ct.p[r] = r < n ? contrib[r] : nullptr;
-  const bool deferred = n > 8 && shard <= ZK_K1_DEFER_MAX_SHARD;
+  const bool deferred = n > 8;
   const int64_t blocks = deferred ? k1_blocks_deferred(shard) : k1_blocks(shard);
+  Partial* partials = (Partial*)workspace_partials(workspace);
+  uint32_t* ticket = (uint32_t*)workspace;
+  int e;
   if (deferred)
-    hipLaunchKernelGGL(k1_reduce_check_deferred, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS),
-                       ZK_K1_DEFER_LDS, stream, ct, n, shard, inv32, grad,
-                       (Partial*)workspace_partials(workspace), (uint32_t*)workspace);
+    e = launch_segments(blocks, ZK_K1_DEFER_SEG_ELEMS / (4 * ZK_K1_THREADS * ZK_K1_DEFER),
+                        [&](int64_t b0, int64_t nb) {
+                          hipLaunchKernelGGL(k1_reduce_check_deferred, dim3((uint32_t)nb),
+                                             dim3(ZK_K1_THREADS), ZK_K1_DEFER_LDS, stream, ct, n,
+                                             shard, inv32, grad, partials, ticket, b0);
+                        });
   else
-    hipLaunchKernelGGL(k1_reduce_check, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), k1_lds(n),
-                       stream, ct, n, shard, inv32, grad, (Partial*)workspace_partials(workspace),
-                       (uint32_t*)workspace);
-  const int e = (int)hipGetLastError();
+    e = launch_segments(blocks, ZK_K1_SEG_ELEMS / (4 * ZK_K1_THREADS * ZK_K1_QUADS),
+                        [&](int64_t b0, int64_t nb) {
+                          hipLaunchKernelGGL(k1_reduce_check, dim3((uint32_t)nb),
+                                             dim3(ZK_K1_THREADS), k1_lds(n), stream, ct, n, shard,
+                                             inv32, grad, partials, ticket, b0);
+                        });
   if (e != hipSuccess) return e;
   return launch_partials_finalize(workspace, blocks, fa, res, stream);
 }
@@ -361,20 +377,24 @@ int launch_finalize_bf16(const FinalizeArgs& fa, zero_step_result_t* res, hipStr
   return (int)hipGetLastError();
 }
 
+constexpr int64_t kK2SegBlocks = ZK_K2_SEG_ELEMS / (4 * ZK_K2_THREADS * ZK_K2_QUADS);
+
 int launch_adam_bf16(const float* grad, float* master, float* m, float* v, uint16_t* slot,
                      int64_t shard, const AdamScalars& sc, const zero_step_result_t* res,
                      hipStream_t stream) {
-  hipLaunchKernelGGL(k2_adam_bf16, dim3((uint32_t)k2_blocks(shard)), dim3(ZK_K2_THREADS), ZK_K2_LDS,
-                     stream, grad, master, m, v, slot, shard, sc, res);
-  return (int)hipGetLastError();
+  return launch_segments(k2_blocks(shard), kK2SegBlocks, [&](int64_t b0, int64_t nb) {
+    hipLaunchKernelGGL(k2_adam_bf16, dim3((uint32_t)nb), dim3(ZK_K2_THREADS), ZK_K2_LDS, stream,
+                       grad, master, m, v, slot, shard, sc, res, b0);
+  });
 }
 
 int launch_adam(const float* grad, float* master, float* m, float* v, uint16_t* slot,
                 int64_t shard, const AdamScalars& sc, const zero_step_result_t* res,
                 hipStream_t stream) {
-  hipLaunchKernelGGL(k2_adam, dim3((uint32_t)k2_blocks(shard)), dim3(ZK_K2_THREADS), ZK_K2_LDS, stream,
-                     grad, master, m, v, slot, shard, sc, res);
-  return (int)hipGetLastError();
+  return launch_segments(k2_blocks(shard), kK2SegBlocks, [&](int64_t b0, int64_t nb) {
+    hipLaunchKernelGGL(k2_adam, dim3((uint32_t)nb), dim3(ZK_K2_THREADS), ZK_K2_LDS, stream,
+                       grad, master, m, v, slot, shard, sc, res, b0);
+  });
 }
 
 }  // namespace zk

@@ -61,10 +61,11 @@ __device__ __forceinline__ int32_t find_unit(int32_t n_units, int64_t b, First f
   return lo;
 }
 
+// b0: the first workgroup of this launch (see launch_segments).
 __global__ __launch_bounds__(ZK_K1_THREADS) void k1u_reduce_check(
     const zero_unit_buffers_t* __restrict__ units, int32_t n_units, int32_t n, float inv32,
-    Partial* __restrict__ partials, uint32_t* __restrict__ ticket) {
-  const int64_t b = blockIdx.x;
+    Partial* __restrict__ partials, uint32_t* __restrict__ ticket, int64_t b0) {
+  const int64_t b = b0 + blockIdx.x;
   if (b == 0 && threadIdx.x == 0) *ticket = 0u;  // arm the finalize kernel's ticket
   const int32_t u = find_unit(n_units, b, [&](int32_t i) { return units[i].reduce_block; });
   const UnitBuffersGlobal& ub = ((const UnitBuffersGlobal*)units)[u];
@@ -85,9 +86,9 @@ __global__ __launch_bounds__(ZK_K1_THREADS) void k1u_reduce_check(
 static_assert(ZK_K1_QUADS == 1, "a chunk is one one-quad workgroup");
 __global__ __launch_bounds__(ZK_K1_THREADS) void k1u_reduce_check_deferred(
     const zero_unit_buffers_t* __restrict__ units, int32_t n_units, int64_t chunks, int32_t n,
-    float inv32, Partial* __restrict__ partials, uint32_t* __restrict__ ticket) {
+    float inv32, Partial* __restrict__ partials, uint32_t* __restrict__ ticket, int64_t b0) {
   constexpr int K = ZK_K1_DEFER;
-  const int64_t b = blockIdx.x;
+  const int64_t b = b0 + blockIdx.x;
   if (b == 0 && threadIdx.x == 0) *ticket = 0u;
   uint64_t qlo = 0, qhi = 0;
   uint32_t bad = 0;
@@ -133,10 +134,10 @@ __global__ __launch_bounds__(ZK_K1_THREADS) void k1u_reduce_check_deferred(
 
 __global__ __launch_bounds__(ZK_K2_THREADS) void k2u_adam(
     const zero_unit_buffers_t* __restrict__ units, int32_t n_units, AdamScalars sc,
-    const zero_step_result_t* __restrict__ res) {
+    const zero_step_result_t* __restrict__ res, int64_t b0) {
   if (res->skip) return;
   const float c = res->clip_coef;
-  const int64_t b = blockIdx.x;
+  const int64_t b = b0 + blockIdx.x;
   const int32_t u = find_unit(n_units, b, [&](int32_t i) { return units[i].adam_block; });
   const UnitBuffersGlobal& ub = ((const UnitBuffersGlobal*)units)[u];
 #pragma unroll
@@ -243,28 +244,37 @@ int launch_units_reduce_adam_1pass(const zero_unit_buffers_t* units_dev,
 }
 
 int launch_units_reduce(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
-                        int64_t elems, int n, float inv32, void* workspace, int64_t* n_partials,
+                        int n, float inv32, void* workspace, int64_t* n_partials,
                         hipStream_t stream) {
   Partial* partials = (Partial*)workspace_partials(workspace);
-  if (n > 8 && elems <= ZK_K1_DEFER_MAX_SHARD) {
+  uint32_t* ticket = (uint32_t*)workspace;
+  if (n > 8) {
     const int64_t wg = (blocks + ZK_K1_DEFER - 1) / ZK_K1_DEFER;
-    hipLaunchKernelGGL(k1u_reduce_check_deferred, dim3((uint32_t)wg), dim3(ZK_K1_THREADS),
-                       ZK_K1_DEFER_LDS, stream, units_dev, n_units, blocks, n, inv32, partials,
-                       (uint32_t*)workspace);
     *n_partials = wg;
-  } else {
-    hipLaunchKernelGGL(k1u_reduce_check, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), k1_lds(n),
-                       stream, units_dev, n_units, n, inv32, partials, (uint32_t*)workspace);
-    *n_partials = blocks;
+    return launch_segments(wg, ZK_K1_DEFER_SEG_ELEMS / (4 * ZK_K1_THREADS * ZK_K1_DEFER),
+                           [&](int64_t b0, int64_t nb) {
+                             hipLaunchKernelGGL(k1u_reduce_check_deferred, dim3((uint32_t)nb),
+                                                dim3(ZK_K1_THREADS), ZK_K1_DEFER_LDS, stream,
+                                                units_dev, n_units, blocks, n, inv32, partials,
+                                                ticket, b0);
+                           });
   }
-  return (int)hipGetLastError();
+  *n_partials = blocks;
+  return launch_segments(blocks, ZK_K1_SEG_ELEMS / (4 * ZK_K1_THREADS * ZK_K1_QUADS),
+                         [&](int64_t b0, int64_t nb) {
+                           hipLaunchKernelGGL(k1u_reduce_check, dim3((uint32_t)nb),
+                                              dim3(ZK_K1_THREADS), k1_lds(n), stream, units_dev,
+                                              n_units, n, inv32, partials, ticket, b0);
+                         });
 }
 
 int launch_units_adam(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
                       const AdamScalars& sc, const zero_step_result_t* res, hipStream_t stream) {
-  hipLaunchKernelGGL(k2u_adam, dim3((uint32_t)blocks), dim3(ZK_K2_THREADS), ZK_K2_LDS, stream, units_dev,
-                     n_units, sc, res);
-  return (int)hipGetLastError();
+  return launch_segments(blocks, ZK_K2_SEG_ELEMS / (4 * ZK_K2_THREADS * ZK_K2_QUADS),
+                         [&](int64_t b0, int64_t nb) {
+                           hipLaunchKernelGGL(k2u_adam, dim3((uint32_t)nb), dim3(ZK_K2_THREADS),
+                                              ZK_K2_LDS, stream, units_dev, n_units, sc, res, b0);
+                         });
 }
 
 }  // namespace zk
