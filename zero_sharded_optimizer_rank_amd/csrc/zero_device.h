@@ -123,6 +123,9 @@
 #ifndef ZK_K2_SEG_ELEMS
 #define ZK_K2_SEG_ELEMS ((int64_t)1 << 27)
 #endif
+#ifndef ZK_K12_SEG_ELEMS
+#define ZK_K12_SEG_ELEMS ((int64_t)1 << 28)
+#endif
 // The single-pass kernel (reduce and update in one pass, steps without
 // clipping) streams N + 3 inputs and 4 outputs.  One-wave workgroups, 16 per
 // CU for N <= 8 and 20 beyond (10240 and 8192 B of reserved LDS).  Measured

@@ -97,37 +97,40 @@ __global__ __launch_bounds__(ZK_K2_THREADS) void k2_adam(
 // `out` state and slot.  KF then finalizes as after K1.
 __global__ __launch_bounds__(ZK_K12_THREADS) void k12_reduce_adam(
     ContribTable ct, int32_t n, int64_t shard, float inv32, StatePair st, AdamScalars sc,
-    Partial* __restrict__ partials, uint32_t* __restrict__ ticket) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
+    Partial* __restrict__ partials, uint32_t* __restrict__ ticket, int64_t b0) {
+  const int64_t b = b0 + blockIdx.x;
+  if (b == 0 && threadIdx.x == 0) *ticket = 0u;
   uint64_t qlo = 0, qhi = 0;
   uint32_t bad = 0;
-  const int64_t qd = (int64_t)blockIdx.x * ZK_K12_THREADS + threadIdx.x;
+  const int64_t qd = b * ZK_K12_THREADS + threadIdx.x;
   reduce_adam_quad(ct, n, shard, qd, inv32, st, sc, qlo, qhi, bad);
   block_reduce<ZK_K12_THREADS>(qlo, qhi, bad);
-  if (threadIdx.x == 0) partials[blockIdx.x] = make_partial(qlo, qhi, bad);
+  if (threadIdx.x == 0) partials[b] = make_partial(qlo, qhi, bad);
 }
 
 // --- bf16 path -------------------------------------------------------------
 __global__ __launch_bounds__(ZK_K1_THREADS) void k1_reduce_check_bf16(
     ContribTable ct, int32_t n, int64_t shard, float inv32, float* __restrict__ grad,
-    Partial* __restrict__ partials, uint32_t* __restrict__ ticket) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;  // arm the tree kernel's ticket
-  const int64_t q_first = (int64_t)blockIdx.x * ZK_K1_THREADS;
+    Partial* __restrict__ partials, uint32_t* __restrict__ ticket, int64_t b0) {
+  const int64_t b = b0 + blockIdx.x;
+  if (b == 0 && threadIdx.x == 0) *ticket = 0u;  // arm the tree kernel's ticket
+  const int64_t q_first = b * ZK_K1_THREADS;
   const Partial pt = reduce_block_bf16(ct, n, shard, q_first, inv32, grad);
-  if (threadIdx.x == 0) partials[blockIdx.x] = pt;
+  if (threadIdx.x == 0) partials[b] = pt;
 }
 
 // K12 in bf16: the single pass with the bf16 tree partial of K1's bf16 form.
 __global__ __launch_bounds__(ZK_K1_THREADS) void k12_reduce_adam_bf16(
     ContribTable ct, int32_t n, int64_t shard, float inv32, StatePair st, AdamScalars sc,
-    Partial* __restrict__ partials, uint32_t* __restrict__ ticket) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
+    Partial* __restrict__ partials, uint32_t* __restrict__ ticket, int64_t b0) {
+  const int64_t b = b0 + blockIdx.x;
+  if (b == 0 && threadIdx.x == 0) *ticket = 0u;
   uint32_t bad = 0;
-  const int64_t qd = (int64_t)blockIdx.x * ZK_K1_THREADS + threadIdx.x;
+  const int64_t qd = b * ZK_K1_THREADS + threadIdx.x;
   double x = reduce_adam_quad_bf16(ct, n, shard, qd, inv32, st, sc, bad);
   block_tree<ZK_K1_THREADS>(x, bad);
   if (threadIdx.x == 0)
-    partials[blockIdx.x] = Partial{(uint64_t)__double_as_longlong(x), (uint64_t)(bad ? 1u : 0u) << 63};
+    partials[b] = Partial{(uint64_t)__double_as_longlong(x), (uint64_t)(bad ? 1u : 0u) << 63};
 }
 
 __global__ __launch_bounds__(kThreads) void kt_tree_finalize_bf16(
@@ -300,10 +303,15 @@ int launch_reduce_adam_1pass(const uint16_t* const* contrib, int n, int64_t shar
   for (int r = 0; r < ZERO_MAX_RANKS; ++r) ct.p[r] = r < n ? contrib[r] : nullptr;
   const StatePair st{master_in, m_in, v_in, master_out, m_out, v_out, slot_out};
   const int64_t blocks = k12_blocks(shard);
-  hipLaunchKernelGGL(k12_reduce_adam, dim3((uint32_t)blocks), dim3(ZK_K12_THREADS), k12_lds(n),
-                     stream, ct, n, shard, inv32, st, sc,
-                     (Partial*)workspace_partials(workspace), (uint32_t*)workspace);
-  const int e = (int)hipGetLastError();
+  Partial* partials = (Partial*)workspace_partials(workspace);
+  uint32_t* ticket = (uint32_t*)workspace;
+  const int e = launch_segments(blocks, ZK_K12_SEG_ELEMS / (4 * ZK_K12_THREADS),
+                                [&](int64_t b0, int64_t nb) {
+                                  hipLaunchKernelGGL(k12_reduce_adam, dim3((uint32_t)nb),
+                                                     dim3(ZK_K12_THREADS), k12_lds(n), stream, ct,
+                                                     n, shard, inv32, st, sc, partials, ticket,
+                                                     b0);
+                                });
   if (e != hipSuccess) return e;
   return launch_partials_finalize(workspace, blocks, fa, res, stream);
 }
@@ -333,9 +341,12 @@ int launch_reduce_check_bf16(const uint16_t* const* contrib, int n, int64_t shar
   const int64_t blocks = k1_blocks_bf16(shard);
   uint32_t* ticket = (uint32_t*)workspace;
   Partial* partials = (Partial*)workspace_partials(workspace);
-  hipLaunchKernelGGL(k1_reduce_check_bf16, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), ZK_K1B_LDS, stream,
-                     ct, n, shard, inv32, grad, partials, ticket);
-  int e = (int)hipGetLastError();
+  const int e = launch_segments(blocks, ZK_K1_SEG_ELEMS / (4 * ZK_K1_THREADS),
+                                [&](int64_t b0, int64_t nb) {
+                                  hipLaunchKernelGGL(k1_reduce_check_bf16, dim3((uint32_t)nb),
+                                                     dim3(ZK_K1_THREADS), ZK_K1B_LDS, stream, ct,
+                                                     n, shard, inv32, grad, partials, ticket, b0);
+                                });
   if (e != hipSuccess) return e;
   return launch_tree_finalize_bf16(workspace, blocks, fa, res, stream);
 }
@@ -350,10 +361,15 @@ int launch_reduce_adam_1pass_bf16(const uint16_t* const* contrib, int n, int64_t
   for (int r = 0; r < ZERO_MAX_RANKS; ++r) ct.p[r] = r < n ? contrib[r] : nullptr;
   const StatePair st{master_in, m_in, v_in, master_out, m_out, v_out, slot_out};
   const int64_t blocks = k1_blocks_bf16(shard);
-  hipLaunchKernelGGL(k12_reduce_adam_bf16, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS),
-                     ZK_K12B_LDS, stream, ct, n, shard, inv32, st, sc,
-                     (Partial*)workspace_partials(workspace), (uint32_t*)workspace);
-  const int e = (int)hipGetLastError();
+  Partial* partials = (Partial*)workspace_partials(workspace);
+  uint32_t* ticket = (uint32_t*)workspace;
+  const int e = launch_segments(blocks, ZK_K12_SEG_ELEMS / (4 * ZK_K1_THREADS),
+                                [&](int64_t b0, int64_t nb) {
+                                  hipLaunchKernelGGL(k12_reduce_adam_bf16, dim3((uint32_t)nb),
+                                                     dim3(ZK_K1_THREADS), ZK_K12B_LDS, stream, ct,
+                                                     n, shard, inv32, st, sc, partials, ticket,
+                                                     b0);
+                                });
   if (e != hipSuccess) return e;
   return launch_tree_finalize_bf16(workspace, blocks, fa, res, stream);
 }

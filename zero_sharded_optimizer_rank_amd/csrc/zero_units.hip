@@ -155,8 +155,8 @@ static_assert(ZK_K1_QUADS == 1, "the unit single pass reuses the reduce's one-qu
 __global__ __launch_bounds__(ZK_K1_THREADS) void k12u_reduce_adam(
     const zero_unit_buffers_t* __restrict__ units, const zero_unit_buffers_t* __restrict__ outs,
     int32_t n_units, int32_t n, float inv32, AdamScalars sc, Partial* __restrict__ partials,
-    uint32_t* __restrict__ ticket) {
-  const int64_t b = blockIdx.x;
+    uint32_t* __restrict__ ticket, int64_t b0) {
+  const int64_t b = b0 + blockIdx.x;
   if (b == 0 && threadIdx.x == 0) *ticket = 0u;
   const int32_t u = find_unit(n_units, b, [&](int32_t i) { return units[i].reduce_block; });
   const UnitBuffersGlobal& ub = ((const UnitBuffersGlobal*)units)[u];
@@ -237,10 +237,15 @@ int launch_units_reduce_adam_1pass(const zero_unit_buffers_t* units_dev,
                                    const zero_unit_buffers_t* outs_dev, int32_t n_units,
                                    int64_t blocks, int n, float inv32, const AdamScalars& sc,
                                    void* workspace, hipStream_t stream) {
-  hipLaunchKernelGGL(k12u_reduce_adam, dim3((uint32_t)blocks), dim3(ZK_K1_THREADS), ZK_K12U_LDS,
-                     stream, units_dev, outs_dev, n_units, n, inv32, sc,
-                     (Partial*)workspace_partials(workspace), (uint32_t*)workspace);
-  return (int)hipGetLastError();
+  Partial* partials = (Partial*)workspace_partials(workspace);
+  uint32_t* ticket = (uint32_t*)workspace;
+  return launch_segments(blocks, ZK_K12_SEG_ELEMS / (4 * ZK_K1_THREADS),
+                         [&](int64_t b0, int64_t nb) {
+                           hipLaunchKernelGGL(k12u_reduce_adam, dim3((uint32_t)nb),
+                                              dim3(ZK_K1_THREADS), ZK_K12U_LDS, stream, units_dev,
+                                              outs_dev, n_units, n, inv32, sc, partials, ticket,
+                                              b0);
+                         });
 }
 
 int launch_units_reduce(const zero_unit_buffers_t* units_dev, int32_t n_units, int64_t blocks,
