@@ -13,8 +13,11 @@ exactly what zero_reduce_adam_step enqueues.  Inputs are resident in HBM when
 the timed region starts; every timed step is applied (no skip).
 
 Prints one JSON line.  Fields beyond the common ones:
-  roofline      the dominant kernel's algorithmic bytes per launch over its
-                average HIP-event duration, against the 8 TB/s HBM peak
+  roofline      the dominant kernel's algorithmic bytes per step over the
+                HIP-event duration of its dispatches in a step (a long grid
+                goes out as several consecutive dispatches), against the
+                8 TB/s HBM peak; `traffic` is the counter-measured HBM bytes of
+                the same dispatches
   kernels       the same figures for both kernels
   cpu_baseline  the CPU oracle timed on bounded windows of the same shard, in
                 one process and in one process per host core (at most 16)
@@ -55,8 +58,8 @@ def bytes_per_param(n: int):
 
 
 def traffic_for(workload: str, kernel: str):
-    """Counter-derived HBM bytes per launch, if recorded for the current
-    kernel source; else None."""
+    """Counter-derived HBM bytes of one step's dispatches of `kernel`, if
+    recorded for the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -65,7 +68,7 @@ def traffic_for(workload: str, kernel: str):
     if rec.get("kernel_hash") != kernel_hash():
         return None
     k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes_per_launch")
+    return None if k is None else k.get("bytes_per_step")
 
 
 def _oracle_inputs(w, begin: int, n: int):
@@ -247,12 +250,22 @@ def summarize_rocprof(label: str, bench_args: str, pmc_args: str, out: str = "gp
             return 30 * S
         return None
 
+    # A long grid goes out as several dispatches of one kernel per step, so
+    # every figure below is per step: the sum over that kernel's dispatches,
+    # divided by the number of steps (one finalize dispatch per step).
     stats = {}
     for r in csv.DictReader(open(_prof_file("*kernel_stats.csv", kt_dir))):
         k = _prof_short(r["Name"])
-        if k is not None:
-            stats[k] = dict(calls=int(r["Calls"]), avg=float(r["AverageNs"]) / 1e3,
-                            mn=float(r["MinNs"]) / 1e3, mx=float(r["MaxNs"]) / 1e3)
+        if k is None:
+            continue
+        calls, avg = int(r["Calls"]), float(r["AverageNs"]) / 1e3
+        v = stats.setdefault(k, dict(calls=0, total=0.0, mn=float("inf"), mx=0.0))
+        v["calls"] += calls
+        v["total"] += calls * avg
+        v["mn"] = min(v["mn"], float(r["MinNs"]) / 1e3)
+        v["mx"] = max(v["mx"], float(r["MaxNs"]) / 1e3)
+    fin = "kt_tree_finalize_bf16" if "kt_tree_finalize_bf16" in stats else "kf_reduce_finalize"
+    steps = stats[fin]["calls"] if fin in stats else 1
 
     def counters(cname):
         d = os.path.join(out, f"prof_{cname}_{label}")
@@ -265,10 +278,14 @@ def summarize_rocprof(label: str, bench_args: str, pmc_args: str, out: str = "gp
                 acc.setdefault(k, []).append(float(r["Counter_Value"]))
         calib = float(_json_line(os.path.join(out, f"bench_{cname}_{label}.log"))
                       ["calibration_copy"]["bytes"])
-        return {k: sum(v) / len(v) for k, v in acc.items()}, calib
+        n_steps = len(acc.get("kt_tree_finalize_bf16", acc.get("kf_reduce_finalize", [0]))) or 1
+        per_step = {k: sum(v) / n_steps for k, v in acc.items() if k != "calib_copy"}
+        per_step["calib_copy"] = sum(acc["calib_copy"]) / len(acc["calib_copy"])
+        per_disp = {k: len(v) / n_steps for k, v in acc.items()}
+        return per_step, per_disp, calib
 
-    fetch, calib_f = counters("FETCH_SIZE")
-    write, calib_w = counters("WRITE_SIZE")
+    fetch, disp_f, calib_f = counters("FETCH_SIZE")
+    write, _, calib_w = counters("WRITE_SIZE")
     fs = calib_f / (fetch["calib_copy"] * 1024)
     ws = calib_w / (write["calib_copy"] * 1024)
     kh = kernel_hash()
@@ -278,8 +295,8 @@ def summarize_rocprof(label: str, bench_args: str, pmc_args: str, out: str = "gp
         if k == "calib_copy":
             continue
         rb, wb = fetch[k] * 1024 * fs, write.get(k, 0.0) * 1024 * ws
-        rec["kernels"][k] = {"read_bytes": rb, "write_bytes": wb, "bytes_per_launch": rb + wb,
-                             "algorithmic_bytes": algo(k)}
+        rec["kernels"][k] = {"read_bytes": rb, "write_bytes": wb, "bytes_per_step": rb + wb,
+                             "dispatches_per_step": disp_f[k], "algorithmic_bytes": algo(k)}
     prof = prof or os.path.join(ROOT, "profiles")
     with open(os.path.join(prof, f"traffic_{label}.json"), "w") as f:
         json.dump(rec, f, indent=1)
@@ -298,40 +315,55 @@ def summarize_rocprof(label: str, bench_args: str, pmc_args: str, out: str = "gp
     calib_kt = (j.get("calibration_copy") or {}).get("bytes")
     with open(os.path.join(prof, f"{prefix}_{label}_kernel_stats.md"), "w") as f:
         f.write(f"# Kernel durations: {desc}\n\n" + recipe +
-                f"Kernel source hash (bench.py `kernel_hash`): `{kh}`.\n\n"
-                "| kernel | calls | avg (us) | min (us) | max (us) | algorithmic bytes / launch "
-                "| GB/s at avg |\n|---|---|---|---|---|---|---|\n")
-        for k, v in sorted(stats.items(), key=lambda kv: -kv[1]["avg"]):
-            a = 2 * calib_kt if (k == "calib_copy" and calib_kt) else algo(k)
-            f.write(f"| {k} | {v['calls']} | {v['avg']:.1f} | {v['mn']:.1f} | {v['mx']:.1f} | "
-                    + (f"{a / 1e9:.3f} GB | {a / (v['avg'] * 1e3):.0f} |" if a else "- | - |")
-                    + "\n")
-        f.write("\nThe JSON line this traced run printed (HIP events on the launch stream):\n\n")
+                f"Kernel source hash (bench.py `kernel_hash`): `{kh}`.  {steps} steps traced "
+                f"(one `{fin}` dispatch each).\n\n"
+                "| kernel | dispatches | per step | avg per dispatch (us) | min (us) | max (us) "
+                "| per step (us) | algorithmic bytes per step | GB/s |\n"
+                "|---|---|---|---|---|---|---|---|---|\n")
+        for k, v in sorted(stats.items(), key=lambda kv: -kv[1]["total"]):
+            avg = v["total"] / v["calls"]
+            if k == "calib_copy":
+                a = 2 * calib_kt if calib_kt else None
+                f.write(f"| {k} | {v['calls']} | - | {avg:.1f} | {v['mn']:.1f} | {v['mx']:.1f} "
+                        f"| - | " + (f"{a / 1e9:.3f} GB per dispatch | {a / (avg * 1e3):.0f} |"
+                                     if a else "- | - |") + "\n")
+                continue
+            per = v["total"] / steps
+            a = algo(k)
+            f.write(f"| {k} | {v['calls']} | {v['calls'] / steps:g} | {avg:.1f} | {v['mn']:.1f} "
+                    f"| {v['mx']:.1f} | {per:.1f} | "
+                    + (f"{a / 1e9:.3f} GB | {a / (per * 1e3):.0f} |" if a else "- | - |") + "\n")
+        f.write("\nThe JSON line this traced run printed (HIP events on the launch stream, "
+                "around all of a kernel's dispatches in a step):\n\n")
         for k, v in j["kernels"].items():
             f.write(f"- {k}: {v['ms'] * 1e3:.1f} us ({v['gbps']:.0f} GB/s)\n")
         f.write(f"- step {j['ms_per_step'] * 1e3:.1f} us, {j['value'] / 1e9:.2f} G params/s\n")
         f.write("\nOnly this library's kernels and the calibration copy (`calib_copy`, a one-shot "
                 "copy of known size) are listed; torch's set-up kernels are left out.  "
-                "The reduce's deferred form (above N = 8, on up to 2^27 elements) is listed "
+                "A long grid is issued as several dispatches of one kernel, so `per step` is "
+                "the dispatch count and the summed duration in one step; GB/s is the step's "
+                "algorithmic bytes over that sum.  "
+                "The reduce's deferred form (above N = 8) is listed "
                 "under the one-chunk kernel's name (`k1_reduce_check`, `k1u_reduce_check`).  "
                 "Algorithmic bytes: 2N + 4 per element for the reduce, 30 for the update, "
                 "2N + 26 for the single pass.\n")
     with open(os.path.join(prof, f"{prefix}_{label}_hbm_traffic.md"), "w") as f:
-        f.write(f"# HBM traffic per launch: {desc}\n\n" + recipe +
-                f"Kernel source hash: `{kh}`.  Counter values are KiB per dispatch, averaged "
-                "over the dispatches.\n\n"
+        f.write(f"# HBM traffic per step: {desc}\n\n" + recipe +
+                f"Kernel source hash: `{kh}`.  Counter values are KiB summed over a kernel's "
+                "dispatches in one step (averaged over the steps).\n\n"
                 f"Calibration: calib_copy moves exactly {calib_f:.0e} bytes each way per call. "
                 f"FETCH_SIZE reads {fetch['calib_copy']:.1f} KiB for it (scale x{fs:.4f}); "
                 f"WRITE_SIZE reads {write['calib_copy']:.1f} KiB (scale x{ws:.4f}).\n\n"
-                "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes (scaled) | write bytes "
-                "(scaled) | total | algorithmic | total / algorithmic |\n"
-                "|---|---|---|---|---|---|---|---|\n")
+                "| kernel | dispatches per step | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes "
+                "(scaled) | write bytes (scaled) | total | algorithmic | total / algorithmic |\n"
+                "|---|---|---|---|---|---|---|---|---|\n")
         for k, v in rec["kernels"].items():
             a = v["algorithmic_bytes"]
-            f.write(f"| {k} | {fetch[k]:.1f} | {write.get(k, 0):.1f} | "
+            f.write(f"| {k} | {v['dispatches_per_step']:g} | {fetch[k]:.1f} | "
+                    f"{write.get(k, 0):.1f} | "
                     f"{v['read_bytes'] / 1e9:.4f} GB | {v['write_bytes'] / 1e9:.4f} GB | "
-                    f"{v['bytes_per_launch'] / 1e9:.4f} GB | "
-                    + (f"{a / 1e9:.4f} GB | {v['bytes_per_launch'] / a:.4f} |" if a
+                    f"{v['bytes_per_step'] / 1e9:.4f} GB | "
+                    + (f"{a / 1e9:.4f} GB | {v['bytes_per_step'] / a:.4f} |" if a
                        else "- | - |") + "\n")
     print(f"wrote profiles for {label}")
 
