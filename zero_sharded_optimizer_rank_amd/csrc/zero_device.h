@@ -109,7 +109,9 @@
 // buffers): the deferred reduce at N = 64 in launches of 2^25 elements
 // against one launch: Llama-2-70B 22.02 against 23.27 ms (one-chunk form),
 // S = 250 M 4.96 / 5.30, the flat 7.5B shard 2.26 / 2.41 (2^24: 2.25, 2^26:
-// 2.31); the one-chunk reduce at N = 8 in launches of 2^28: 3.08 against
+// 2.31); built into the kernels, 2^26 / 2^25 / 2^24 / 2^23 per launch took
+// 22.39 / 21.90 / 21.68 / 21.64 ms on Llama-2-70B and 2.30 / 2.25 / 2.22 /
+// 2.22 on the flat 7.5B shard; the one-chunk reduce at N = 8 in launches of 2^28: 3.08 against
 // 3.16 ms (2^27: 3.12, 2^26: 3.18; shorter ones lose to the launch gaps);
 // the update in launches of 2^26-2^28: 4.55 against 4.60 ms.  A plain copy
 // gains nothing from it (6.73 against 6.71 TB/s in two launches, less in
@@ -118,13 +120,19 @@
 #define ZK_K1_SEG_ELEMS ((int64_t)1 << 28)
 #endif
 #ifndef ZK_K1_DEFER_SEG_ELEMS
-#define ZK_K1_DEFER_SEG_ELEMS ((int64_t)1 << 25)
+#define ZK_K1_DEFER_SEG_ELEMS ((int64_t)1 << 24)
 #endif
 #ifndef ZK_K2_SEG_ELEMS
 #define ZK_K2_SEG_ELEMS ((int64_t)1 << 27)
 #endif
+// The single pass: 2^26 elements per launch for N <= 8, 2^23 beyond (flat
+// 7.5B at N = 64: one launch 3.15 ms, 2^24 2.98, 2^23 2.94, 2^22 2.93;
+// Llama-3-8B: 2^28 6.67, 2^26 6.63, 2^24 6.82).
 #ifndef ZK_K12_SEG_ELEMS
-#define ZK_K12_SEG_ELEMS ((int64_t)1 << 28)
+#define ZK_K12_SEG_ELEMS ((int64_t)1 << 26)
+#endif
+#ifndef ZK_K12_SEG_ELEMS_LARGE_N
+#define ZK_K12_SEG_ELEMS_LARGE_N ((int64_t)1 << 23)
 #endif
 // The single-pass kernel (reduce and update in one pass, steps without
 // clipping) streams N + 3 inputs and 4 outputs.  One-wave workgroups, 16 per
@@ -170,10 +178,16 @@ inline unsigned k12_lds(int n) { return n <= 8 ? ZK_K12_LDS_SMALL_N : ZK_K12_LDS
 
 // Issue a one-shot grid of `blocks` workgroups as launches of at most `seg`
 // workgroups each, in order on one stream: launch(b0, nb) launches
-// workgroups b0 .. b0 + nb - 1 (the kernels add b0 to blockIdx.x).
+// workgroups b0 .. b0 + nb - 1 (the kernels add b0 to blockIdx.x).  A grid
+// of up to two segments goes out whole: on short shards the gaps between
+// launches cost more than the split gains (GPT-2's 24 M elements at N = 64:
+// deferred reduce in one launch 0.497 ms, in launches of 2^24 0.512).
+inline int64_t k12_seg_elems(int n) { return n > 8 ? ZK_K12_SEG_ELEMS_LARGE_N : ZK_K12_SEG_ELEMS; }
+
 template <typename Launch>
 inline int launch_segments(int64_t blocks, int64_t seg, Launch launch) {
   if (seg < 1) seg = 1;
+  if (blocks <= 2 * seg) seg = blocks > 0 ? blocks : 1;
   for (int64_t b0 = 0; b0 < blocks; b0 += seg) {
     launch(b0, blocks - b0 < seg ? blocks - b0 : seg);
     const hipError_t e = hipGetLastError();

@@ -305,7 +305,7 @@ int launch_reduce_adam_1pass(const uint16_t* const* contrib, int n, int64_t shar
   const int64_t blocks = k12_blocks(shard);
   Partial* partials = (Partial*)workspace_partials(workspace);
   uint32_t* ticket = (uint32_t*)workspace;
-  const int e = launch_segments(blocks, ZK_K12_SEG_ELEMS / (4 * ZK_K12_THREADS),
+  const int e = launch_segments(blocks, k12_seg_elems(n) / (4 * ZK_K12_THREADS),
                                 [&](int64_t b0, int64_t nb) {
                                   hipLaunchKernelGGL(k12_reduce_adam, dim3((uint32_t)nb),
                                                      dim3(ZK_K12_THREADS), k12_lds(n), stream, ct,
@@ -363,7 +363,7 @@ int launch_reduce_adam_1pass_bf16(const uint16_t* const* contrib, int n, int64_t
   const int64_t blocks = k1_blocks_bf16(shard);
   Partial* partials = (Partial*)workspace_partials(workspace);
   uint32_t* ticket = (uint32_t*)workspace;
-  const int e = launch_segments(blocks, ZK_K12_SEG_ELEMS / (4 * ZK_K1_THREADS),
+  const int e = launch_segments(blocks, k12_seg_elems(n) / (4 * ZK_K1_THREADS),
                                 [&](int64_t b0, int64_t nb) {
                                   hipLaunchKernelGGL(k12_reduce_adam_bf16, dim3((uint32_t)nb),
                                                      dim3(ZK_K1_THREADS), ZK_K12B_LDS, stream, ct,

@@ -239,7 +239,7 @@ int launch_units_reduce_adam_1pass(const zero_unit_buffers_t* units_dev,
                                    void* workspace, hipStream_t stream) {
   Partial* partials = (Partial*)workspace_partials(workspace);
   uint32_t* ticket = (uint32_t*)workspace;
-  return launch_segments(blocks, ZK_K12_SEG_ELEMS / (4 * ZK_K1_THREADS),
+  return launch_segments(blocks, k12_seg_elems(n) / (4 * ZK_K1_THREADS),
                          [&](int64_t b0, int64_t nb) {
                            hipLaunchKernelGGL(k12u_reduce_adam, dim3((uint32_t)nb),
                                               dim3(ZK_K1_THREADS), ZK_K12U_LDS, stream, units_dev,
