@@ -305,11 +305,11 @@ int zero_reduce_adam_step_noalloc(const zero_plan_t* plan, int32_t rank,
  * the pass and calls zero_finalize with the other ranks' values; the skip it
  * writes then decides the adoption on every rank alike.
  * When to use it: it saves the gradient's round trip (8 of 2N + 34 bytes per
- * element), which pays at small N (Llama-3-8B at N = 8: 6.74 ms against
- * 7.70 ms on an MI355X).  At N = 64 the contribution rows are 83% of its bytes
- * and its mixed stream of 67 inputs and 4 outputs runs about 8% below the
- * reduce's rate, so the two-pass step is as fast or faster there (GPT-2
- * shard 0.641 against 0.649 ms, flat 7.5B shard 3.00 against 3.15 ms): use
+ * element), which pays at small N (Llama-3-8B at N = 8: 6.62 ms against
+ * 7.59 ms on an MI355X).  At N = 64 the contribution rows are 83% of its bytes
+ * and its mixed stream of 67 inputs and 4 outputs runs about 10% below the
+ * reduce's rate, so the two-pass step is faster there (GPT-2 shard 0.60
+ * against 0.64 ms, flat 7.5B shard 2.75 against 2.93 ms): use
  * zero_reduce_adam_step above N = 8.
  * Errors: as zero_reduce_adam_step, plus ZERO_EINVAL for max_grad_norm > 0,
  * for an out buffer that overlaps an in buffer, and for out buffers that
