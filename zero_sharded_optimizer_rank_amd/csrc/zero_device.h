@@ -104,18 +104,18 @@
 #endif
 // Elements per launch of the streaming kernels.  A one-shot grid streams
 // more slowly the longer it runs; the same workgroups issued as several
-// launches back to back on the stream (launch_segments) run faster.  Each
-// form was measured through windows of one shard (interleaved, same
-// buffers): the deferred reduce at N = 64 in launches of 2^25 elements
-// against one launch: Llama-2-70B 22.02 against 23.27 ms (one-chunk form),
-// S = 250 M 4.96 / 5.30, the flat 7.5B shard 2.26 / 2.41 (2^24: 2.25, 2^26:
-// 2.31); built into the kernels, 2^26 / 2^25 / 2^24 / 2^23 per launch took
-// 22.39 / 21.90 / 21.68 / 21.64 ms on Llama-2-70B and 2.30 / 2.25 / 2.22 /
-// 2.22 on the flat 7.5B shard; the one-chunk reduce at N = 8 in launches of 2^28: 3.08 against
-// 3.16 ms (2^27: 3.12, 2^26: 3.18; shorter ones lose to the launch gaps);
-// the update in launches of 2^26-2^28: 4.55 against 4.60 ms.  A plain copy
-// gains nothing from it (6.73 against 6.71 TB/s in two launches, less in
-// more).
+// launches back to back on the stream (launch_segments) run faster.  First
+// measured through windows of one shard (interleaved, same buffers): the
+// deferred reduce at N = 64 in launches of 2^25 elements against one
+// launch: Llama-2-70B 22.02 against 23.27 ms (one-chunk form), S = 250 M
+// 4.96 / 5.30, the flat 7.5B shard 2.26 / 2.41 (2^24: 2.25, 2^26: 2.31);
+// built into the kernels, 2^26 / 2^25 / 2^24 / 2^23 per launch took 22.39 /
+// 21.90 / 21.68 / 21.64 ms on Llama-2-70B and 2.30 / 2.25 / 2.22 / 2.22 on
+// the flat 7.5B shard.  The one-chunk reduce at N = 8 in launches of 2^28:
+// 3.08 against 3.16 ms (2^27: 3.12, 2^26: 3.18; shorter ones lose to the
+// launch gaps); the update in launches of 2^26-2^28: 4.55 against 4.60 ms.
+// A plain copy gains nothing from it (6.73 against 6.71 TB/s in two
+// launches, less in more).
 #ifndef ZK_K1_SEG_ELEMS
 #define ZK_K1_SEG_ELEMS ((int64_t)1 << 28)
 #endif

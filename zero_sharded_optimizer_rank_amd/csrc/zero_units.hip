@@ -1,5 +1,6 @@
-// Multi-unit form of the shard step (ZeRO-3 / FSDP): one launch of the
-// reduce and one of the Adam kernel update every unit a rank holds.
+// Multi-unit form of the shard step (ZeRO-3 / FSDP): one grid of the reduce
+// and one of the Adam kernel (each issued as consecutive launches when it is
+// long, see launch_segments) update every unit a rank holds.
 //
 // Pages: "10.6 ZeRO 与 FSDP" §10.6.4 (stage 3: each GPU updates its 1/N of
 // the parameters from its 1/N of the optimizer state and of the gradient) and
